@@ -1,0 +1,93 @@
+/*
+ * Plain CPU oracle for draft-tree construction.  TEST INFRASTRUCTURE ONLY:
+ * it exists so the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark can check and time the HIP library against an obviously correct
+ * implementation.  The product path never calls it.
+ *
+ * What it computes, in the order the method states it:
+ *  - DART (arXiv 2601.19278), Fig. 3 caption: the d logits of one drafter
+ *    forward each propose the token of one tree depth ("candidate tokens are
+ *    selected from the corresponding position's predicted logit"), an N-gram
+ *    model keeps only continuations that stay continuous, and the pruned tree
+ *    is verified with tree attention.
+ *  - DARTree (llmdb page, "Tree Construction" and its equation; scholarbro
+ *    abstract): a fixed-width candidate tree of depth K and width W, all
+ *    candidates of a depth scored in one batch with a path-conditioned score,
+ *    the top-W across the whole frontier kept after every depth, then
+ *    best-first pruning selects the verification tree.
+ *
+ * Readings where the pages are silent (each also listed in the design doc):
+ *  - the N-gram is a hard filter, keep iff logp > min_logp (strict); with
+ *    min_logp = -INFINITY sparse tables test membership only;
+ *  - continuity is checked at every depth, depth 1 against the committed
+ *    context ctx[b] = (t_-2, t_-1);
+ *  - the ranked score is the cumulative path log-probability
+ *    S = sum(x - lse) (+ g in DARTree mode), g = E[parent_tok] . F[child_tok];
+ *    within a depth the lse-free key Rk = sum(x) (+ g) orders candidates
+ *    identically and is what is sorted;
+ *  - ties: top-k by (x desc, id asc); frontier by (Rk desc, token asc,
+ *    parent rank asc); budget by (S desc, depth asc, BFS index asc);
+ *  - children with x = -inf (probability zero) are never expanded;
+ *  - the budget counts draft nodes (root excluded).
+ *
+ * All arithmetic is double precision.  Logits are read exactly (bf16 widened
+ * by a 16-bit shift).  NaN logits are undefined.
+ */
+#ifndef DT_ORACLE_H
+#define DT_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_NGRAM_NONE 0
+#define ORACLE_NGRAM_DENSE_BIGRAM 1
+#define ORACLE_NGRAM_CSR_BIGRAM 2
+#define ORACLE_NGRAM_HASH_TRIGRAM 3
+
+#define ORACLE_MODE_DART 0
+#define ORACLE_MODE_DARTREE 1
+
+typedef struct oracle_ngram {
+    int32_t kind;
+    float min_logp;
+    const float* dense_logp;    /* [V][V] */
+    const int32_t* row_ptr;     /* [V+1] */
+    const int32_t* col;         /* [nnz] */
+    const float* csr_logp;      /* [nnz] */
+    const uint64_t* keys;       /* [cap], 0xFFFF..FF = empty */
+    const int32_t* succ;        /* [cap][S], -1 = none */
+    const float* hash_logp;     /* [cap][S] */
+    int64_t cap;
+    int32_t S;
+} oracle_ngram;
+
+/* log-softmax normaliser of one row: m + log(sum exp(x - m)), -inf if every
+ * entry is -inf. */
+double oracle_row_lse(const void* row, int is_bf16, int64_t V);
+
+/* The k largest entries of one row by (value desc, id asc): ids and values. */
+void oracle_row_topk(const void* row, int is_bf16, int64_t V, int k,
+                     int32_t* tok, double* val);
+
+/* Does the N-gram admit child token c after context (t2, t1)?  (t2 is only
+ * used by the trigram.) */
+int oracle_continuity(const oracle_ngram* ng, int64_t V, int32_t t2, int32_t t1, int32_t c);
+
+/* The whole path for B requests.  Outputs are [B][budget] (mask
+ * [B][budget][ceil(budget/32)]); rows past n_nodes hold token -1,
+ * parent -1, depth 0, score -inf and a zero mask row.  lookups (optional,
+ * [B]) receives the number of N-gram lookups made (one per expanded node).
+ * Returns 0, or -1 on invalid arguments. */
+int oracle_build_tree(const void* logits, int is_bf16, int B, int64_t V, int d, int k,
+                      int W, int budget, int mode, const int32_t* ctx,
+                      const float* E, const float* F, int R, const oracle_ngram* ng,
+                      int32_t* n_nodes, int32_t* tokens, int32_t* parents,
+                      int32_t* depths, float* scores, uint32_t* mask, int64_t* lookups);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
