@@ -1,0 +1,271 @@
+// C entry points of libdt.so (declared and documented in include/dt.h):
+// host-side validation, launch planning and the two kernel launches.
+// Nothing here allocates, synchronises or keeps state between calls.
+#include <math.h>
+
+#include "common.h"
+
+namespace dt {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
+
+SweepPlan plan_sweep(const dt_params* p) {
+    SweepPlan s{};
+    s.rows = (int64_t)p->B * p->d;
+    const int V = p->V;
+    int C;
+    if (p->sweep_chunks > 0) {
+        C = p->sweep_chunks;
+    } else {
+        // at least ~two 256-thread workgroups per CU (256 CUs), chunks of
+        // >= 4096 elements, and a cross-chunk merge of <= kMergeKeysPerRow keys
+        const int64_t target = 512;
+        int64_t c = s.rows >= target ? 1 : ceil_div(target, s.rows > 0 ? s.rows : 1);
+        const int64_t by_len = V / 4096 > 1 ? V / 4096 : 1;
+        const int64_t by_merge = kMergeKeysPerRow / p->k;
+        if (c > by_len) c = by_len;
+        if (c > by_merge) c = by_merge;
+        C = (int)(c < 1 ? 1 : c);
+    }
+    if (C > V) C = V;
+    s.chunk = (int)round_up(ceil_div(V, C), 8);
+    s.C = (int)ceil_div(V, s.chunk);
+    return s;
+}
+
+WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s) {
+    WorkspacePlan w{};
+    const int64_t n = s.rows * s.C;
+    w.off_m = 0;
+    w.off_s = (size_t)round_up(n * 4, 256);
+    w.off_keys = (size_t)round_up((int64_t)w.off_s + n * 8, 256);
+    w.total = (size_t)round_up((int64_t)w.off_keys + n * p->k * 8, 256);
+    if (n == 0) w.total = 0;
+    return w;
+}
+
+TreePlan plan_tree(const dt_params* p, int kind) {
+    TreePlan P{};
+    const int d = p->d, k = p->k, W = p->W;
+    if (kind == DT_NGRAM_NONE) P.n_ctx = 0;
+    else if (kind == DT_NGRAM_HASH_TRIGRAM) P.n_ctx = d == 1 ? 1 : 1 + k + (d - 2) * k * k;
+    else P.n_ctx = 1 + (d - 1) * k;
+    P.max_nodes = d * W;
+    P.max_cand = W * k;
+    int off = 0;
+    auto take = [&](int bytes, int align) {
+        off = (int)round_up(off, align);
+        const int o = off;
+        off += bytes;
+        return o;
+    };
+    P.off_lse = take(d * 8, 8);
+    P.off_g = take(p->mode == DT_MODE_DARTREE ? d * k * k * 8 : 0, 8);
+    P.off_ttok = take(d * k * 4, 4);
+    P.off_tx = take(d * k * 4, 4);
+    P.off_ctxbase = 0;
+    P.off_vmask = take(P.n_ctx * 4, 4);
+    P.off_misc = take(16 * 4, 4);
+    // node and candidate arrays; the per-wave merge scratch of step 1 reuses this space
+    const int region = (int)round_up(off, 16);
+    off = region;
+    const int nn = P.max_nodes, nc = P.max_cand;
+    P.off_nodes = region;
+    P.off_n_rk = take(nn * 8, 8);
+    P.off_n_s = take(nn * 8, 8);
+    P.off_cand = off;
+    P.off_c_rk = take(nc * 8, 8);
+    P.off_c_s = take(nc * 8, 8);
+    P.off_rowmax = take(W * 8, 8);
+    P.off_n_tok = take(nn * 4, 4);
+    P.off_n_par = take(nn * 4, 4);
+    P.off_n_dep = take(nn * 4, 4);
+    P.off_n_tidx = take(nn * 4, 4);
+    P.off_n_cctx = take(nn * 4, 4);
+    P.off_n_new = take(nn * 4, 4);
+    P.off_n_out = take(nn * 4, 4);
+    P.off_c_tie = take(nc * 4, 4);
+    P.off_c_surv = take(nc * 4, 4);
+    P.off_merge = region;
+    const int merge_end = region + kWaves * kMergeKeysPerRow * 8;
+    P.total = (int)round_up(off > merge_end ? off : merge_end, 16);
+    return P;
+}
+
+// ---------------------------------------------------------------------------
+// validation (host only; no HIP call)
+// ---------------------------------------------------------------------------
+static dt_status check_shape(const dt_params* p) {
+    if (!p) return DT_ERR_INVALID_ARG;
+    if (p->B < 0 || p->d < 1 || p->k < 1 || p->V < 1 || p->W < 1 || p->budget < 1)
+        return DT_ERR_INVALID_ARG;
+    if (p->k > p->V) return DT_ERR_INVALID_ARG;
+    if (p->dtype != DT_DTYPE_F32 && p->dtype != DT_DTYPE_BF16) return DT_ERR_INVALID_ARG;
+    if (p->mode != DT_MODE_DART && p->mode != DT_MODE_DARTREE) return DT_ERR_INVALID_ARG;
+    if (p->sweep_chunks < 0) return DT_ERR_INVALID_ARG;
+    if (p->d > kMaxD || p->k > kMaxK || p->W > kMaxW || p->budget > kMaxBudget ||
+        p->W * p->k > kMaxCandidates || p->V >= kMaxV)
+        return DT_ERR_UNSUPPORTED;
+    const SweepPlan s = plan_sweep(p);
+    if ((int64_t)s.C * p->k > kMergeKeysPerRow) return DT_ERR_UNSUPPORTED;
+    return DT_OK;
+}
+
+static dt_status check_workspace(const dt_params* p) {
+    const WorkspacePlan w = plan_workspace(p, plan_sweep(p));
+    if (w.total == 0) return DT_OK;
+    if (!p->workspace || ((uintptr_t)p->workspace & 15u) || p->workspace_bytes < w.total)
+        return DT_ERR_WORKSPACE;
+    return DT_OK;
+}
+
+static dt_status check_ngram(const dt_ngram_table* g) {
+    if (!g) return DT_ERR_INVALID_ARG;
+    const bool finite = !(isinf(g->min_logp) && g->min_logp < 0);
+    if (isnan(g->min_logp)) return DT_ERR_INVALID_ARG;
+    switch (g->kind) {
+    case DT_NGRAM_NONE:
+        return DT_OK;
+    case DT_NGRAM_DENSE_BIGRAM:
+        return g->dense_logp ? DT_OK : DT_ERR_INVALID_ARG;
+    case DT_NGRAM_CSR_BIGRAM:
+        if (!g->row_ptr || !g->col || (finite && !g->csr_logp)) return DT_ERR_INVALID_ARG;
+        return DT_OK;
+    case DT_NGRAM_HASH_TRIGRAM:
+        if (!g->keys || !g->succ || (finite && !g->hash_logp)) return DT_ERR_INVALID_ARG;
+        if (g->cap < 2 || (g->cap & (g->cap - 1)) != 0) return DT_ERR_INVALID_ARG;
+        if (g->S < 1 || g->S > 64) return DT_ERR_UNSUPPORTED;
+        return DT_OK;
+    default:
+        return DT_ERR_INVALID_ARG;
+    }
+}
+
+}  // namespace dt
+
+using namespace dt;
+
+extern "C" const char* dt_status_string(dt_status s) {
+    switch (s) {
+    case DT_OK: return "DT_OK";
+    case DT_ERR_INVALID_ARG: return "DT_ERR_INVALID_ARG: null pointer, value out of range or misaligned buffer";
+    case DT_ERR_UNSUPPORTED: return "DT_ERR_UNSUPPORTED: outside the limits of this build";
+    case DT_ERR_WORKSPACE: return "DT_ERR_WORKSPACE: workspace missing, misaligned or smaller than dt_workspace_size()";
+    case DT_ERR_HIP: return "DT_ERR_HIP: the HIP runtime refused a launch";
+    default: return "unknown dt_status";
+    }
+}
+
+extern "C" size_t dt_workspace_size(const dt_params* p) {
+    if (check_shape(p) != DT_OK) return 0;
+    return plan_workspace(p, plan_sweep(p)).total;
+}
+
+static dt_status launch_sweep_for(const void* logits, const dt_params* p, const SweepPlan& s,
+                                  const WorkspacePlan& w) {
+    hipStream_t stream = (hipStream_t)p->stream;
+    char* ws = (char*)p->workspace;
+    SweepArgs sa{};
+    sa.logits = logits;
+    sa.V = p->V;
+    sa.C = s.C;
+    sa.chunk = s.chunk;
+    sa.k = p->k;
+    sa.part_m = (float*)(ws + w.off_m);
+    sa.part_s = (double*)(ws + w.off_s);
+    sa.part_keys = (unsigned long long*)(ws + w.off_keys);
+    if (p->prof_event_start && hipEventRecord((hipEvent_t)p->prof_event_start, stream) != hipSuccess)
+        return DT_ERR_HIP;
+    if (launch_sweep(sa, s.rows, p->dtype, stream) != hipSuccess) return DT_ERR_HIP;
+    if (p->prof_event_stop && hipEventRecord((hipEvent_t)p->prof_event_stop, stream) != hipSuccess)
+        return DT_ERR_HIP;
+    return DT_OK;
+}
+
+extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngram,
+                                   const dt_params* p, const dt_tree_out* out) {
+    dt_status st = check_shape(p);
+    if (st != DT_OK) return st;
+    if ((st = check_ngram(ngram)) != DT_OK) return st;
+    if (!out) return DT_ERR_INVALID_ARG;
+    if (p->mode == DT_MODE_DARTREE) {
+        if (!p->E || !p->F) return DT_ERR_INVALID_ARG;
+        if (p->R < 4 || p->R > 256 || p->R % 4 != 0) return DT_ERR_UNSUPPORTED;
+    }
+    const TreePlan plan = plan_tree(p, ngram->kind);
+    if (plan.total > kTreeLdsLimit) return DT_ERR_UNSUPPORTED;
+    if (p->B == 0) return DT_OK;
+    if (!logits || ((uintptr_t)logits & 15u) || !p->ctx) return DT_ERR_INVALID_ARG;
+    if (!out->n_nodes || !out->tokens || !out->parents || !out->depths || !out->scores || !out->mask)
+        return DT_ERR_INVALID_ARG;
+    if ((st = check_workspace(p)) != DT_OK) return st;
+
+    const SweepPlan s = plan_sweep(p);
+    const WorkspacePlan w = plan_workspace(p, s);
+    if ((st = launch_sweep_for(logits, p, s, w)) != DT_OK) return st;
+
+    char* ws = (char*)p->workspace;
+    TreeArgs ta{};
+    ta.B = p->B;
+    ta.V = p->V;
+    ta.d = p->d;
+    ta.k = p->k;
+    ta.W = p->W;
+    ta.budget = p->budget;
+    ta.mode = p->mode;
+    ta.C = s.C;
+    ta.R = p->R;
+    ta.mask_words = (p->budget + 31) / 32;
+    ta.ctx = p->ctx;
+    ta.part_m = (const float*)(ws + w.off_m);
+    ta.part_s = (const double*)(ws + w.off_s);
+    ta.part_keys = (const unsigned long long*)(ws + w.off_keys);
+    ta.ng_kind = ngram->kind;
+    ta.min_logp = ngram->min_logp;
+    ta.dense = ngram->dense_logp;
+    ta.row_ptr = ngram->row_ptr;
+    ta.col = ngram->col;
+    ta.csr_logp = ngram->csr_logp;
+    ta.keys = (const unsigned long long*)ngram->keys;
+    ta.succ = ngram->succ;
+    ta.hash_logp = ngram->hash_logp;
+    ta.cap = ngram->cap;
+    ta.S = ngram->S;
+    ta.E = p->E;
+    ta.F = p->F;
+    ta.n_nodes = out->n_nodes;
+    ta.tokens = out->tokens;
+    ta.parents = out->parents;
+    ta.depths = out->depths;
+    ta.scores = out->scores;
+    ta.mask = out->mask;
+    ta.plan = plan;
+    if (launch_tree(ta, (hipStream_t)p->stream) != hipSuccess) return DT_ERR_HIP;
+    return DT_OK;
+}
+
+extern "C" dt_status dt_position_topk(const void* logits, const dt_params* p, double* lse,
+                                      int32_t* topk_tok, float* topk_val) {
+    dt_status st = check_shape(p);
+    if (st != DT_OK) return st;
+    if (p->B == 0) return DT_OK;
+    if (!logits || ((uintptr_t)logits & 15u) || !lse || !topk_tok || !topk_val) return DT_ERR_INVALID_ARG;
+    if ((st = check_workspace(p)) != DT_OK) return st;
+    const SweepPlan s = plan_sweep(p);
+    const WorkspacePlan w = plan_workspace(p, s);
+    if ((st = launch_sweep_for(logits, p, s, w)) != DT_OK) return st;
+    char* ws = (char*)p->workspace;
+    MergeArgs ma{};
+    ma.rows = (int)s.rows;
+    ma.C = s.C;
+    ma.k = p->k;
+    ma.part_m = (const float*)(ws + w.off_m);
+    ma.part_s = (const double*)(ws + w.off_s);
+    ma.part_keys = (const unsigned long long*)(ws + w.off_keys);
+    ma.lse = lse;
+    ma.tok = topk_tok;
+    ma.val = topk_val;
+    if (launch_merge(ma, (hipStream_t)p->stream) != hipSuccess) return DT_ERR_HIP;
+    return DT_OK;
+}

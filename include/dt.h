@@ -1,0 +1,192 @@
+/*
+ * dt.h -- C ABI of libdt.so: draft-tree construction on AMD Instinct MI355X
+ * (gfx950) for diffusion-style speculative decoding.
+ *
+ * The operation (one call = one batch of B independent requests):
+ *
+ *   d per-position draft logit rows  --->  pruned draft token tree + mask
+ *
+ * as the pages define it:
+ *   - DART (arXiv 2601.19278), Fig. 3 caption ("Continuity-Aware Tree
+ *     Pruning"): the drafter's d logits come from one forward with d-1 mask
+ *     tokens ("shifted logits prediction"), the first from the last prefix
+ *     position; candidate tokens of each depth are taken from that
+ *     position's own logit; an N-gram model keeps only expansions that stay
+ *     continuous; the pruned tree is verified with tree attention.
+ *   - DARTree (llmdb page, "Tree Construction" and its P_AR equation;
+ *     scholarbro abstract): a fixed-width candidate tree of depth K and
+ *     width W, every candidate of a depth scored in one batch with a
+ *     path-conditioned score, the top-W kept across the whole frontier after
+ *     each depth, then best-first pruning selects the verification tree.
+ *
+ * Concretely, for request b:
+ *   1. lse_i = log sum_v exp(logits[b][i][v]) and T_i = the k largest
+ *      logits of row i, ordered (value desc, token id asc), i = 0..d-1.
+ *   2. The root is the last committed token ctx[b][1] (context ctx[b][0],
+ *      ctx[b][1]).  For depth t = 1..d every frontier node p of depth t-1
+ *      is paired with every child c in T_{t-1}.  The pair is kept iff
+ *      logits[b][t-1][c] > -inf and the N-gram admits c after p's context
+ *      (bigram: p's token; trigram: (p's parent's token, p's token), the
+ *      root using ctx[b][0]); an admitted entry needs logp > min_logp
+ *      (strict), and min_logp = -INFINITY tests membership only.
+ *   3. Each kept child gets Rk = (Rk_p + x) + g and S = (S_p + (x - lse)) + g
+ *      in double precision, x = its logit, g = E[tok_p] . F[c] in DARTREE
+ *      mode (the low-rank parent-conditioned term), g = 0 in DART mode.
+ *      The frontier of depth t is the first min(W, #kept) candidates in the
+ *      order (Rk desc, token asc, parent's frontier rank asc).  Growth stops
+ *      at the first empty frontier.
+ *   4. If the candidate tree has more than `budget` nodes, best-first
+ *      selection repeatedly takes the available node (parent already taken,
+ *      or depth 1) with the best (S desc, depth asc, BFS index asc) until
+ *      `budget` nodes are taken.
+ *   5. Output in BFS order (depth asc, then frontier rank).
+ *
+ * Output tree (caller-allocated device memory, n_max = budget,
+ * mask_words = ceil(budget / 32)):
+ *   n_nodes [B]                     int32, number of draft nodes (0..budget)
+ *   tokens  [B][n_max]              int32, token id, -1 in padding rows
+ *   parents [B][n_max]              int32, parent node index, -1 = the root
+ *   depths  [B][n_max]              int32, 1..d, 0 in padding rows
+ *   scores  [B][n_max]              float, S rounded to fp32, -inf padding
+ *   mask    [B][n_max][mask_words]  uint32, row i has bit j (word j >> 5,
+ *                                   bit j & 31, LSB first) set iff node j
+ *                                   is node i or one of its ancestors; the
+ *                                   root and prefix are implicit; padding
+ *                                   rows are zero.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers unless stated otherwise; the
+ *     structs themselves are host memory read during the call only.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     never allocates, frees or synchronises, and keeps no state between
+ *     calls.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns without waiting.  Calls on different
+ *     streams need different workspaces.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     an error nothing is enqueued and no output is touched.  A launch
+ *     failure returns DT_ERR_HIP.  Faults during execution surface at the
+ *     caller's next synchronisation of `stream`.
+ *   - Logits are finite or -inf.  NaN or +inf logits give unspecified
+ *     (but memory-safe) results.  ctx ids must lie in [0, V); other values
+ *     admit no children under bigram tables and add no parent term.  Table
+ *     contents (row_ptr ranges, successor ids) are trusted as given.
+ *   - Limits: B >= 0; 1 <= d <= 32; 1 <= k <= 32 and k <= V; 1 <= W <= 64;
+ *     W * k <= 1024; 1 <= budget <= 1024; 1 <= V < 2^26; the logits
+ *     pointer 16-byte aligned; and the tree kernel's shared-memory plan
+ *     (which grows with d, k, W, the N-gram kind and the mode) must fit in
+ *     64 KiB, else DT_ERR_UNSUPPORTED.  DARTREE mode needs E and F with
+ *     R a multiple of 4, 4 <= R <= 256.
+ */
+#ifndef DT_H
+#define DT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dt_status {
+    DT_OK = 0,
+    DT_ERR_INVALID_ARG = 1,   /* a null pointer, a value out of range, a misaligned buffer */
+    DT_ERR_UNSUPPORTED = 2,   /* valid but outside this build's limits (see above) */
+    DT_ERR_WORKSPACE = 3,     /* workspace missing or smaller than dt_workspace_size() */
+    DT_ERR_HIP = 4            /* the HIP runtime refused a launch */
+} dt_status;
+
+typedef enum dt_dtype { DT_DTYPE_F32 = 0, DT_DTYPE_BF16 = 1 } dt_dtype;
+
+typedef enum dt_mode {
+    DT_MODE_DART = 0,      /* score = cumulative draft log-probability */
+    DT_MODE_DARTREE = 1    /* + parent-conditioned term E[parent] . F[child] */
+} dt_mode;
+
+typedef enum dt_ngram_kind {
+    DT_NGRAM_NONE = 0,          /* every expansion is continuous */
+    DT_NGRAM_DENSE_BIGRAM = 1,  /* logp[V][V] indexed [parent token][child] */
+    DT_NGRAM_CSR_BIGRAM = 2,    /* successors of a token, ascending ids */
+    DT_NGRAM_HASH_TRIGRAM = 3   /* open-addressing table keyed by (t_-2, t_-1) */
+} dt_ngram_kind;
+
+/* N-gram continuity table (device arrays; unused fields may be NULL).
+ *  dense:  dense_logp[V][V] float.
+ *  CSR:    row_ptr[V+1] int32, col[nnz] int32 ascending within a row,
+ *          csr_logp[nnz] float (may be NULL when min_logp = -INFINITY).
+ *  hash:   keys[cap] uint64 with key = (uint64)t_-2 << 32 | (uint32)t_-1 and
+ *          0xFFFFFFFFFFFFFFFF marking a free slot; a key lives in the first
+ *          free slot at or after splitmix64(key) & (cap - 1) (the SplitMix64
+ *          output function of Steele, Lea and Flood), probing linearly with
+ *          wrap-around; succ[cap][S] int32 successor ids, -1 = none;
+ *          hash_logp[cap][S] float (may be NULL when min_logp = -INFINITY).
+ *          cap is a power of two with at least one free slot, 1 <= S <= 64. */
+typedef struct dt_ngram_table {
+    int32_t kind;              /* dt_ngram_kind */
+    float min_logp;            /* keep iff logp > min_logp; -INFINITY = membership */
+    const float* dense_logp;
+    const int32_t* row_ptr;
+    const int32_t* col;
+    const float* csr_logp;
+    int64_t nnz;
+    const uint64_t* keys;
+    const int32_t* succ;
+    const float* hash_logp;
+    int64_t cap;
+    int32_t S;
+} dt_ngram_table;
+
+typedef struct dt_params {
+    int32_t B;                 /* requests in the batch */
+    int32_t V;                 /* vocabulary size (row length) */
+    int32_t d;                 /* draft positions = tree depth (K in DARTree) */
+    int32_t k;                 /* candidates taken from each position's logit */
+    int32_t W;                 /* frontier width kept per depth */
+    int32_t budget;            /* verification budget = n_max rows of the output */
+    int32_t dtype;             /* dt_dtype of the logits */
+    int32_t mode;              /* dt_mode */
+    const int32_t* ctx;        /* [B][2] device: (t_-2, t_-1), t_-1 is the root */
+    const float* E;            /* [V][R] device, DARTREE only (else may be NULL) */
+    const float* F;            /* [V][R] device, DARTREE only */
+    int32_t R;                 /* rank of E and F */
+    int32_t sweep_chunks;      /* 0 = automatic; else split each row into this many chunks */
+    void* workspace;           /* device scratch of at least dt_workspace_size() bytes */
+    size_t workspace_bytes;
+    void* stream;              /* hipStream_t */
+    void* prof_event_start;    /* optional hipEvent_t recorded on `stream` right before */
+    void* prof_event_stop;     /* ... and right after the vocabulary-sweep kernel */
+} dt_params;
+
+typedef struct dt_tree_out {
+    int32_t* n_nodes;          /* [B] */
+    int32_t* tokens;           /* [B][budget] */
+    int32_t* parents;          /* [B][budget] */
+    int32_t* depths;           /* [B][budget] */
+    float* scores;             /* [B][budget] */
+    uint32_t* mask;            /* [B][budget][ceil(budget/32)] */
+} dt_tree_out;
+
+/* The whole path (steps 1-5 above) for B requests.
+ * logits: device [B][d][V] of dtype, rows contiguous, 16-byte aligned. */
+dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngram,
+                        const dt_params* params, const dt_tree_out* out);
+
+/* Bytes of workspace dt_build_tree / dt_position_topk need for these
+ * parameters (depends on B, V, d, k, dtype and sweep_chunks only); 0 if the
+ * parameters are invalid. */
+size_t dt_workspace_size(const dt_params* params);
+
+/* Static, human-readable name of a status code. */
+const char* dt_status_string(dt_status s);
+
+/* Step 1 alone (DART Fig. 3: each position's own logit proposes the tokens
+ * of its depth): per row (b, i) the log-softmax normaliser and the top-k.
+ * lse: device [B][d] double; topk_tok: device [B][d][k] int32 in order
+ * (value desc, id asc); topk_val: device [B][d][k] float (the logits).
+ * Uses B, V, d, k, dtype, sweep_chunks, workspace and stream of params. */
+dt_status dt_position_topk(const void* logits, const dt_params* params,
+                           double* lse, int32_t* topk_tok, float* topk_val);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DT_H */

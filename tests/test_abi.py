@@ -1,0 +1,132 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/dt.h declares, and rejects invalid arguments on the host
+before anything is enqueued (no compute call is made here)."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dt.h")
+
+bd = pytest.importorskip("draft_tree_construction_dt_amd.binding")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dt_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(bd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", bd.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (dt_\w+)", out))
+    assert set(_declared()) <= exported
+    lib = ctypes.CDLL(bd.library_path())
+    for name in _declared():
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c():
+    src = '#include "dt.h"\nint main(void){dt_params p={0}; (void)p; return (int)dt_workspace_size(0);}\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I" + os.path.dirname(HEADER),
+                        "-x", "c", "-"], input=src, text=True, capture_output=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings():
+    for s in range(5):
+        assert bd.dt_status_string(s).startswith("DT_")
+    assert "unknown" in bd.dt_status_string(99)
+
+
+FAKE = 0x100000          # a 16-byte aligned non-null address never dereferenced by validation
+
+
+def _params(**kw):
+    base = dict(B=2, V=1000, d=4, k=5, W=4, budget=10, dtype=bd.DT_DTYPE_BF16, mode=bd.DT_MODE_DART)
+    base.update(kw)
+    return bd.Params(**base)
+
+
+def _call(params, ngram=None, logits=FAKE, out=None, workspace=True):
+    p = params._c()
+    p.ctx = FAKE
+    if workspace:
+        p.workspace = FAKE
+        p.workspace_bytes = 1 << 30
+    g = (ngram or bd.NGram())._c()
+    o = out or bd._TreeOut(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    return bd._load().dt_build_tree(logits, ctypes.byref(g), ctypes.byref(p), ctypes.byref(o))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), bd.DT_ERR_INVALID_ARG),
+    (dict(d=0), bd.DT_ERR_INVALID_ARG),
+    (dict(k=0), bd.DT_ERR_INVALID_ARG),
+    (dict(k=1001), bd.DT_ERR_INVALID_ARG),
+    (dict(W=0), bd.DT_ERR_INVALID_ARG),
+    (dict(budget=0), bd.DT_ERR_INVALID_ARG),
+    (dict(dtype=7), bd.DT_ERR_INVALID_ARG),
+    (dict(mode=3), bd.DT_ERR_INVALID_ARG),
+    (dict(sweep_chunks=-2), bd.DT_ERR_INVALID_ARG),
+    (dict(k=33), bd.DT_ERR_UNSUPPORTED),
+    (dict(W=65), bd.DT_ERR_UNSUPPORTED),
+    (dict(W=64, k=17), bd.DT_ERR_UNSUPPORTED),
+    (dict(d=33), bd.DT_ERR_UNSUPPORTED),
+    (dict(budget=1025), bd.DT_ERR_UNSUPPORTED),
+    (dict(V=1 << 26), bd.DT_ERR_UNSUPPORTED),
+    (dict(sweep_chunks=200, k=5), bd.DT_ERR_UNSUPPORTED),
+    (dict(mode=bd.DT_MODE_DARTREE), bd.DT_ERR_INVALID_ARG),             # E, F missing
+    (dict(mode=bd.DT_MODE_DARTREE, E=FAKE, F=FAKE, R=6), bd.DT_ERR_UNSUPPORTED),
+    (dict(d=32, W=64, k=16), bd.DT_ERR_UNSUPPORTED),                    # shared-memory plan too big
+])
+def test_invalid_parameters(kw, status):
+    assert _call(_params(**kw)) == status
+
+
+def test_invalid_tables_and_buffers():
+    P = _params()
+    assert _call(P, bd.NGram(kind=9)) == bd.DT_ERR_INVALID_ARG
+    assert _call(P, bd.NGram(kind=bd.DT_NGRAM_DENSE_BIGRAM)) == bd.DT_ERR_INVALID_ARG
+    assert _call(P, bd.NGram(kind=bd.DT_NGRAM_CSR_BIGRAM, row_ptr=FAKE)) == bd.DT_ERR_INVALID_ARG
+    assert _call(P, bd.NGram(kind=bd.DT_NGRAM_CSR_BIGRAM, row_ptr=FAKE, col=FAKE, min_logp=-2.0)) == \
+        bd.DT_ERR_INVALID_ARG                                            # finite threshold needs logp
+    hk = dict(kind=bd.DT_NGRAM_HASH_TRIGRAM, keys=FAKE, succ=FAKE, S=16)
+    assert _call(P, bd.NGram(cap=1000, **hk)) == bd.DT_ERR_INVALID_ARG      # not a power of two
+    assert _call(P, bd.NGram(cap=1024, **dict(hk, S=65))) == bd.DT_ERR_UNSUPPORTED
+    assert _call(P, bd.NGram(min_logp=math.nan)) == bd.DT_ERR_INVALID_ARG
+    assert _call(P, logits=FAKE + 4) == bd.DT_ERR_INVALID_ARG               # misaligned logits
+    assert _call(P, logits=0) == bd.DT_ERR_INVALID_ARG
+    assert _call(P, out=bd._TreeOut(FAKE, 0, FAKE, FAKE, FAKE, FAKE)) == bd.DT_ERR_INVALID_ARG
+    assert _call(P, workspace=False) == bd.DT_ERR_WORKSPACE
+
+
+def test_workspace_size_depends_on_shape_only():
+    a = bd.dt_workspace_size(_params(B=64, V=151936, d=8, k=10))
+    b = bd.dt_workspace_size(_params(B=64, V=151936, d=8, k=10, W=2, budget=3))
+    assert a == b > 0
+    assert bd.dt_workspace_size(_params(k=0)) == 0
+    assert bd.dt_workspace_size(_params(B=0)) == 0
+
+
+def test_position_topk_validation():
+    p = _params()._c()
+    p.workspace = FAKE
+    p.workspace_bytes = 1 << 30
+    f = bd._load().dt_position_topk
+    assert f(FAKE, ctypes.byref(p), 0, FAKE, FAKE) == bd.DT_ERR_INVALID_ARG
+    p.k = 40
+    assert f(FAKE, ctypes.byref(p), FAKE, FAKE, FAKE) == bd.DT_ERR_UNSUPPORTED
+    p.k = 5
+    p.workspace_bytes = 8
+    assert f(FAKE, ctypes.byref(p), FAKE, FAKE, FAKE) == bd.DT_ERR_WORKSPACE
