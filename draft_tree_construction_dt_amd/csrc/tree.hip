@@ -330,8 +330,8 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
                 acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {                          // D[4*(lane/16)+q][lane%16]
-                const int ii = ti * 16 + 4 * (lane >> 4) + q, jj = tj * 16 + (lane & 15);
+            for (int q = 0; q < 4; ++q) {                          // D[lane/16 + 4q][lane%16]
+                const int ii = ti * 16 + (lane >> 4) + 4 * q, jj = tj * 16 + (lane & 15);
                 if (ii < kp && jj < k) s_g[((t - 1) * k + ii) * k + jj] = acc[q];
             }
         }
@@ -417,21 +417,21 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
             const int c = e / tpc, part = e - c * tpc;
             int r = 0;
             int slot = -1;
+            bool live = false;
             if (c < ns) {
                 slot = filter ? c_surv[c] : c;
                 const double my = c_rk[slot];
                 const uint32_t mt = c_tie[slot];
-                if (my != -INFINITY) {
+                live = my != -INFINITY;
+                if (live) {
                     for (int q = part; q < ns; q += tpc) {
                         const int o = filter ? c_surv[q] : q;
                         r += cand_before(c_rk[o], c_tie[o], my, mt);
                     }
-                } else {
-                    r = 1 << 30;
                 }
             }
             for (int off = 1; off < tpc; off <<= 1) r += __shfl_xor(r, off);
-            if (c < ns && part == 0 && r < keep) {
+            if (live && part == 0 && r < keep) {
                 const int p = slot / k, j = slot - p * k;
                 const int nd = nb + r;
                 n_tok[nd] = s_ttok[(t - 1) * k + j];
