@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Throughput of draft-tree construction on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one dt_build_tree call on the batched Qwen3-vocab workload: B=64
+independent requests, V=151936, d=8 draft positions, top-k 10, width 8,
+budget 64, bf16 logits (N(0,3) plus a log Zipf(1.1) prior, coherence-planted),
+a shared open-addressing trigram table of 2^22 slots with 16 successors.
+Inputs rotate over several distinct sets totalling more than three times
+the 256 MB Infinity Cache, all resident in HBM before timing starts.  The
+single-request case (B=1, same shape) is timed as well and reported under
+"b1".  Prints one JSON line.
+
+Roofline: the vocabulary sweep kernel dominates; its duration is measured
+live with HIP events that the library records around that kernel on the
+launch stream, and its algorithmic bytes are the logits it must read
+(B*d*V*2 per launch) plus the partials it writes.
+"""
+
+import argparse
+import copy
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "draft trees/sec and µs/tree (B=1, B=64) at V=151936, d=8; % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+BATCH = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_traffic.json")
+SWEEP_SOURCES = [os.path.join(ROOT, "draft_tree_construction_dt_amd", "csrc", f)
+                 for f in ("sweep.hip", "common.h")]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--sets", type=int, default=5, help="distinct B=64 input sets to rotate over")
+    ap.add_argument("--b1-steps", type=int, default=2000, help="timed single-request calls")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="requests the oracle builds for cpu_baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def make_workload(n_sets: int, seed: int = 0):
+    """The benchmark's inputs: n_sets * 64 coherence-planted Qwen3-vocab
+    requests sharing one trigram table; set s is requests [64 s, 64 s + 64)."""
+    from draft_tree_construction_dt_amd import synth
+    return synth.make_problem("c4p", seed, B=BATCH * n_sets)
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    for f in SWEEP_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per sweep launch from committed rocprofv3 counter runs, or
+    None when absent or taken on a different version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sources_sha256") != kernel_sources_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_probe(mib: int) -> None:
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures the single-GPU path only; --gpus must be 1 "
+              "(requests shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+
+    import torch
+    from draft_tree_construction_dt_amd import binding as bd
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    prob = make_workload(args.sets, args.seed)
+    gen_s = time.time() - t0
+    print(f"[bench] generated {args.sets} input sets in {gen_s:.1f}s", file=sys.stderr, flush=True)
+
+    logits = bd.logits_tensor(prob, dev)                      # [sets*64][d][V] bf16
+    ctx = torch.from_numpy(prob.ctx).to(dev)
+    ngram = bd.upload_ngram(prob.ngram, dev)
+    stream = torch.cuda.current_stream()
+    lib = bd._load()
+    fn = lib.dt_build_tree
+
+    def params(B, first):
+        p = bd.Params(B=B, V=prob.V, d=prob.d, k=prob.k, W=prob.W, budget=prob.budget,
+                      dtype=bd.DT_DTYPE_BF16, mode=bd.DT_MODE_DART, ctx=ctx[first:first + B], stream=stream)
+        p.workspace = torch.empty(max(bd.dt_workspace_size(p), 16), dtype=torch.uint8, device=dev)
+        return p
+
+    # ---- B = 64: rotate over the sets
+    sets = [params(BATCH, s * BATCH) for s in range(args.sets)]
+    out = bd.alloc_tree_out(BATCH, prob.budget, dev)
+    ng_c, out_c = ngram._c(), out._c()
+    set_c = [s._c() for s in sets]
+    set_ptr = [logits[s * BATCH].data_ptr() for s in range(args.sets)]
+    logit_bytes = BATCH * prob.d * prob.V * 2
+    for i in range(args.warmup):
+        st = fn(set_ptr[i % args.sets], ctypes.byref(ng_c), ctypes.byref(set_c[i % args.sets]),
+                ctypes.byref(out_c))
+        if st != 0:
+            raise bd.DtError(st, "dt_build_tree")
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:                                            # create the HIP events
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    raw = [(a.cuda_event, b.cuda_event) for a, b in ev]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        pc = set_c[i % args.sets]
+        pc.prof_event_start, pc.prof_event_stop = raw[i]
+        fn(set_ptr[i % args.sets], ctypes.byref(ng_c), ctypes.byref(pc), ctypes.byref(out_c))
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    for pc in set_c:
+        pc.prof_event_start = pc.prof_event_stop = None
+    sweep_ms = [a.elapsed_time(b) for a, b in ev]
+    sweep_avg_s = sum(sweep_ms) / len(sweep_ms) / 1e3
+    ms_per_step = t_total / K * 1e3
+    trees_per_s = BATCH * K / t_total
+
+    # ---- B = 1: one request per call, rotating over every request of every set
+    nreq = BATCH * args.sets
+    one = [params(1, r) for r in range(nreq)]
+    out1 = bd.alloc_tree_out(1, prob.budget, dev)
+    out1_c = out1._c()
+    one_c = [q._c() for q in one]
+    one_ptr = [logits[r].data_ptr() for r in range(nreq)]
+    for i in range(min(200, args.b1_steps)):
+        fn(one_ptr[i % nreq], ctypes.byref(ng_c), ctypes.byref(one_c[i % nreq]), ctypes.byref(out1_c))
+    torch.cuda.synchronize()
+    K1 = args.b1_steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t1 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K1):
+        fn(one_ptr[i % nreq], ctypes.byref(ng_c), ctypes.byref(one_c[i % nreq]), ctypes.byref(out1_c))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    b1_wall = time.perf_counter() - t1
+    b1_gpu_ms = e0.elapsed_time(e1)
+
+    achieved = logit_bytes / sweep_avg_s / 1e9
+    traffic = stored_traffic()
+    res = {
+        "metric": METRIC,
+        "value": trees_per_s,
+        "unit": "trees/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "batched Qwen3-vocab draft trees: B=64, V=151936, d=8, k=10, W=8, budget=64, "
+                        "bf16 logits N(0,3)+log Zipf(1.1) prior with coherence planting, shared "
+                        "trigram table 2^22 slots x 16 successors (DART mode)",
+            "B": BATCH, "V": prob.V, "d": prob.d, "k": prob.k, "W": prob.W, "budget": prob.budget,
+            "logits": "bf16", "input_sets": args.sets,
+            "input_bytes_rotated": logit_bytes * args.sets,
+        },
+        "us_per_tree": t_total / (BATCH * K) * 1e6,
+        "b1": {
+            "workload": "same shape, B=1 (one request per call)",
+            "trees_per_s": K1 / b1_wall,
+            "us_per_tree_wall": b1_wall / K1 * 1e6,
+            "us_per_tree_gpu": b1_gpu_ms / K1 * 1e3,
+            "steps": K1,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "sweep_kernel<bf16>",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "avg_launch_us": sweep_avg_s * 1e6,
+            "algorithmic_bytes_per_launch": logit_bytes,
+        },
+    }
+
+    if not args.no_cpu:
+        import oracle
+        n = min(args.cpu_sample, BATCH)
+        sample = copy.copy(prob)
+        sample.B = n
+        sample.logits = prob.logits[:n]
+        sample.ctx = prob.ctx[:n]
+        tc = time.perf_counter()
+        oracle.build_tree(sample)
+        cpu_s = time.perf_counter() - tc
+        res["cpu_baseline"] = {
+            "value": n / cpu_s,
+            "unit": "trees/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the first {n} requests of input set 0 (whole path: normaliser, top-k, "
+                      f"trigram expansion, top-W, budget, mask), single-threaded C, {cpu_s:.1f}s",
+        }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

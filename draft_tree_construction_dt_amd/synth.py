@@ -246,21 +246,21 @@ class _Ids:
 
 
 def _distinct_rows(rng: np.random.Generator, ids: _Ids, n: int, S: int) -> np.ndarray:
-    """n rows of S distinct ids each."""
-    rows = ids.draw(rng, (n, S))
+    """n rows of S distinct ids each (ascending within a row): duplicates are
+    redrawn until none remain."""
+    rows = np.sort(ids.draw(rng, (n, S)), axis=1)
     todo = np.arange(n)
     while todo.size:
-        sub = np.sort(rows[todo], axis=1)
+        sub = rows[todo]
         dup = np.zeros_like(sub, dtype=bool)
         dup[:, 1:] = sub[:, 1:] == sub[:, :-1]
         bad = dup.any(axis=1)
-        sub_bad = sub[bad]
-        dup_bad = dup[bad]
-        fresh = ids.draw(rng, sub_bad.shape)
-        sub_bad[dup_bad] = fresh[dup_bad]
-        sub[bad] = sub_bad
-        rows[todo] = sub
+        if not bad.any():
+            break
         todo = todo[bad]
+        sub, dup = sub[bad], dup[bad]
+        sub[dup] = ids.draw(rng, int(dup.sum()))
+        rows[todo] = np.sort(sub, axis=1)
     return rows
 
 
@@ -432,9 +432,11 @@ def _plant_hash(ng: NGramTable, plans: list) -> None:
 # ----------------------------------------------------------------------------
 
 def _streams(cfg: Config, seed: int):
+    """Independent streams: one per request (request b's stream does not
+    depend on B), one for the table, one for the embedding tables."""
     root = np.random.SeedSequence([int(seed), zlib.crc32(cfg.name.encode())])
-    kids = root.spawn(cfg.B + 2)
-    return kids[: cfg.B], kids[cfg.B], kids[cfg.B + 1]
+    req_root, tab, ef = root.spawn(3)
+    return req_root.spawn(cfg.B), tab, ef
 
 
 def make_logits(cfg: Config, seed: int, ids_for_plant: Optional[_Ids] = None):

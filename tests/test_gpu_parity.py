@@ -220,3 +220,29 @@ def test_deterministic_across_calls_and_streams(device, oracle_lib):
     for key in a:
         assert np.array_equal(a[key], b[key]), key
     assert not check_invariants(p, a)
+
+
+def test_bench_workload_sampled(device, oracle_lib):
+    """The benchmark's own inputs in its launch configuration (B=64 per call,
+    automatic chunking): sampled requests of two sets against the oracle."""
+    import copy
+    import bench
+    from draft_tree_construction_dt_amd import binding as bd
+    import torch
+    prob = bench.make_workload(2, 0)
+    for s in (0, 1):
+        sub = copy.copy(prob)
+        sub.B = bench.BATCH
+        sub.logits = prob.logits[s * bench.BATCH:(s + 1) * bench.BATCH]
+        sub.ctx = prob.ctx[s * bench.BATCH:(s + 1) * bench.BATCH]
+        _say(f"[case] bench workload set {s}")
+        gpu = run_gpu(sub, device)
+        pick = [0, 7, 13, 29, 31, 42, 58, 63]
+        samp = copy.copy(sub)
+        samp.B = len(pick)
+        samp.logits = sub.logits[pick]
+        samp.ctx = sub.ctx[pick]
+        ora = oracle_lib.build_tree(samp)
+        g = {k: v[pick] for k, v in gpu.items()}
+        assert_parity(samp, g, ora, label=f"bench set {s}")
+        assert not check_invariants(sub, gpu)
