@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests the oracle builds for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sweep-chunks", type=int, default=0, help="0 = the library's automatic plan")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -122,7 +123,8 @@ def main():
 
     def params(B, first):
         p = bd.Params(B=B, V=prob.V, d=prob.d, k=prob.k, W=prob.W, budget=prob.budget,
-                      dtype=bd.DT_DTYPE_BF16, mode=bd.DT_MODE_DART, ctx=ctx[first:first + B], stream=stream)
+                      dtype=bd.DT_DTYPE_BF16, mode=bd.DT_MODE_DART, ctx=ctx[first:first + B], stream=stream,
+                      sweep_chunks=args.sweep_chunks if B > 1 else 0)
         p.workspace = torch.empty(max(bd.dt_workspace_size(p), 16), dtype=torch.uint8, device=dev)
         return p
 

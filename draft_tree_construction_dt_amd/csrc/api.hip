@@ -66,18 +66,14 @@ TreePlan plan_tree(const dt_params* p, int kind) {
     P.off_tx = take(d * k * 4, 4);
     P.off_ctxbase = 0;
     P.off_vmask = take(P.n_ctx * 4, 4);
-    P.off_misc = take(16 * 4, 4);
-    // node and candidate arrays; the per-wave merge scratch of step 1 reuses this space
+    P.off_misc = take(kMiscInts * 4, 4);
+    // node arrays; the per-wave merge scratch of step 1 reuses this space
     const int region = (int)round_up(off, 16);
     off = region;
-    const int nn = P.max_nodes, nc = P.max_cand;
+    const int nn = P.max_nodes;
     P.off_nodes = region;
     P.off_n_rk = take(nn * 8, 8);
     P.off_n_s = take(nn * 8, 8);
-    P.off_cand = off;
-    P.off_c_rk = take(nc * 8, 8);
-    P.off_c_s = take(nc * 8, 8);
-    P.off_rowmax = take(W * 8, 8);
     P.off_n_tok = take(nn * 4, 4);
     P.off_n_par = take(nn * 4, 4);
     P.off_n_dep = take(nn * 4, 4);
@@ -85,10 +81,8 @@ TreePlan plan_tree(const dt_params* p, int kind) {
     P.off_n_cctx = take(nn * 4, 4);
     P.off_n_new = take(nn * 4, 4);
     P.off_n_out = take(nn * 4, 4);
-    P.off_c_tie = take(nc * 4, 4);
-    P.off_c_surv = take(nc * 4, 4);
     P.off_merge = region;
-    const int merge_end = region + kWaves * kMergeKeysPerRow * 8;
+    const int merge_end = region + kMergeWaves * kMergeKeysPerRow * 8;
     P.total = (int)round_up(off > merge_end ? off : merge_end, 16);
     return P;
 }
@@ -136,6 +130,7 @@ static dt_status check_ngram(const dt_ngram_table* g) {
         if (!g->keys || !g->succ || (finite && !g->hash_logp)) return DT_ERR_INVALID_ARG;
         if (g->cap < 2 || (g->cap & (g->cap - 1)) != 0) return DT_ERR_INVALID_ARG;
         if (g->S < 1 || g->S > 64) return DT_ERR_UNSUPPORTED;
+        if (((uintptr_t)g->keys & 15u) != 0) return DT_ERR_INVALID_ARG;
         return DT_OK;
     default:
         return DT_ERR_INVALID_ARG;
@@ -192,6 +187,7 @@ extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngr
     if (p->mode == DT_MODE_DARTREE) {
         if (!p->E || !p->F) return DT_ERR_INVALID_ARG;
         if (p->R < 4 || p->R > 256 || p->R % 4 != 0) return DT_ERR_UNSUPPORTED;
+        if (((uintptr_t)p->E & 15u) || ((uintptr_t)p->F & 15u)) return DT_ERR_INVALID_ARG;
     }
     const TreePlan plan = plan_tree(p, ngram->kind);
     if (plan.total > kTreeLdsLimit) return DT_ERR_UNSUPPORTED;

@@ -15,8 +15,12 @@ constexpr int kMaxD = 32;
 constexpr int kMaxBudget = 1024;
 constexpr int kMaxCandidates = 1024;   // W * k
 constexpr int kMaxV = 1 << 26;         // token ids fit the 26-bit field of the tie key
-constexpr int kThreads = 256;          // both kernels: four wave64s
+constexpr int kThreads = 256;          // sweep and merge kernels: four wave64s
 constexpr int kWaves = kThreads / 64;
+constexpr int kTreeThreads = 1024;     // tree kernel: sixteen wave64s per request
+constexpr int kTreeWaves = kTreeThreads / 64;
+constexpr int kMergeWaves = 8;         // tree-kernel waves that merge the sweep partials
+constexpr int kMiscInts = 32;          // tree-kernel counters (0..3) and scan scratch (16..31)
 constexpr int kTreeLdsLimit = 64 * 1024;
 constexpr int kMergeKeysPerRow = 256;  // C * k bound: per-wave merge scratch in the tree kernel
 constexpr int kSweepVecsPerThread = 4; // 16-byte vectors each thread holds per batch
@@ -70,9 +74,7 @@ struct TreePlan {
     int off_nodes;      // node arrays (aliased by the merge scratch)
     int off_n_tok, off_n_par, off_n_dep, off_n_tidx, off_n_cctx, off_n_new, off_n_out;
     int off_n_rk, off_n_s;
-    int off_cand;       // candidate arrays
-    int off_c_rk, off_c_s, off_c_tie, off_c_src, off_c_surv, off_rowmax;
-    int off_merge;      // uint64 [kWaves][kMergeKeysPerRow] (aliases nodes + candidates)
+    int off_merge;      // uint64 [kMergeWaves][kMergeKeysPerRow] (aliases the node arrays)
     int off_misc;       // int counters
     int total;
 };

@@ -39,7 +39,7 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 }
 
 // k-th largest of one float per lane (bitonic sort across the wave, descending).
-__device__ float wave_kth_largest(float v, int k, int lane) {
+__device__ __forceinline__ float wave_kth_largest(float v, int k, int lane) {
 #pragma unroll
     for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
@@ -65,7 +65,7 @@ struct WaveState {
 // Keep the k largest keys of buf[0..cnt), sorted descending, and raise the
 // threshold to the k-th.  Rank by counting: every entry counts the entries
 // with a larger key (keys are unique: ids differ).
-__device__ void wave_select(unsigned long long* buf, WaveState& st, int k, int lane) {
+__device__ __forceinline__ void wave_select(unsigned long long* buf, WaveState& st, int k, int lane) {
     const int n = st.cnt;
     const unsigned long long a = lane < n ? buf[lane] : 0ull;
     const unsigned long long b = lane + 64 < n ? buf[lane + 64] : 0ull;

@@ -1,4 +1,4 @@
-// Tree construction: one 256-thread workgroup per request, all state in LDS.
+// Tree construction: one 1024-thread workgroup per request, all state in LDS.
 //
 //  1. Merge the sweep's per-chunk partials of the request's d rows into the
 //     log-softmax normaliser (fp64 merge and log) and the exact top-k list
@@ -17,7 +17,8 @@
 //     key Rk and the cumulative log-score S in fp64; the top-W across the
 //     whole frontier by (Rk desc, token asc, parent rank asc) become the next
 //     frontier (DARTree: "selects the top-W scored nodes across the entire
-//     frontier").  No global memory is touched inside the loop.
+//     frontier").  Keys live in registers, ranks come from wave ballots, and
+//     no global memory is touched inside the loop.
 //  4. Budget: best-first selection of the verification tree (DARTree
 //     abstract).  In DART mode S never increases along a path, so the
 //     best-first set equals the top-`budget` nodes by (S desc, BFS index);
@@ -135,6 +136,49 @@ __device__ __forceinline__ bool logp_keeps(const TreeArgs& a, const float* lp, i
     return a.min_logp == -INFINITY || lp == nullptr || lp[e] > a.min_logp;
 }
 
+// Slot of a trigram key, or -1.  Linear probing from splitmix64(key): the
+// aligned group of 8 slots holding the probe position is read with four
+// 16-byte loads, so a chain costs one memory round trip per 8 slots.
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ long long find_slot(const TreeArgs& a, unsigned long long key) {
+    const unsigned long long cm = (unsigned long long)a.cap - 1ull;
+    unsigned long long pos = mix64(key) & cm;
+    if (a.cap < 8) {
+        for (long long probe = 0; probe < a.cap; ++probe) {
+            const unsigned long long here = a.keys[pos];
+            if (here == key) return (long long)pos;
+            if (here == kEmptyKey) return -1;
+            pos = (pos + 1ull) & cm;
+        }
+        return -1;
+    }
+    for (long long seen = 0; seen < a.cap; seen += 8) {
+        const unsigned long long base = pos & ~7ull;
+        const u64x2* g = reinterpret_cast<const u64x2*>(a.keys + base);
+        const u64x2 q0 = g[0], q1 = g[1], q2 = g[2], q3 = g[3];
+        const unsigned long long kk[8] = {q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+        const int start = (int)(pos - base);
+        int hit = -1;
+        bool stop = false;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (!stop && s >= start) {
+                if (kk[s] == key) {
+                    hit = s;
+                    stop = true;
+                } else if (kk[s] == kEmptyKey) {
+                    stop = true;
+                }
+            }
+        }
+        if (hit >= 0) return (long long)(base + hit);
+        if (stop) return -1;
+        pos = (base + 8ull) & cm;
+    }
+    return -1;
+}
+
 // Bit j set iff child T_{t-1}[j] (finite logit) is admitted after (a2, a1).
 __device__ uint32_t admitted_children(const TreeArgs& a, int a2, int a1, const int* ch, const float* cx) {
     const int k = a.k;
@@ -171,22 +215,21 @@ __device__ uint32_t admitted_children(const TreeArgs& a, int a2, int a1, const i
         }
     } else if (a.ng_kind == DT_NGRAM_HASH_TRIGRAM) {
         const unsigned long long key = ((unsigned long long)(uint32_t)a2 << 32) | (uint32_t)a1;
-        const unsigned long long cm = (unsigned long long)a.cap - 1ull;
-        unsigned long long slot = mix64(key) & cm;
-        bool found = false;
-        for (long long probe = 0; probe < a.cap; ++probe) {
-            const unsigned long long here = a.keys[slot];
-            if (here == key) { found = true; break; }
-            if (here == kEmptyKey) break;
-            slot = (slot + 1ull) & cm;
-        }
-        if (!found) return 0;
-        const int* succ = a.succ + (int64_t)slot * a.S;
-        for (int s = 0; s < a.S; ++s) {
-            const int c = succ[s];
-            if (c < 0) continue;
-            for (int j = 0; j < k; ++j)
-                if (ch[j] == c && logp_keeps(a, a.hash_logp, (int64_t)slot * a.S + s)) m |= 1u << j;
+        const long long slot = find_slot(a, key);
+        if (slot < 0) return 0;
+        const int* succ = a.succ + slot * a.S;
+        const bool membership = a.min_logp == -INFINITY || a.hash_logp == nullptr;
+        for (int s0 = 0; s0 < a.S; s0 += 16) {
+            int reg[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) reg[u] = s0 + u < a.S ? succ[s0 + u] : -1;
+            for (int j = 0; j < k; ++j) {
+                const int c = ch[j];
+                int hs = -1;
+#pragma unroll
+                for (int u = 0; u < 16; ++u) hs = reg[u] == c ? s0 + u : hs;
+                if (hs >= 0 && (membership || a.hash_logp[slot * a.S + hs] > a.min_logp)) m |= 1u << j;
+            }
         }
     } else {
         m = live;
@@ -218,12 +261,19 @@ __device__ __forceinline__ bool node_before(double s_a, int i_a, double s_b, int
     return s_a > s_b || (s_a == s_b && i_a < i_b);
 }
 
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
 template <typename T>
 __device__ __forceinline__ T* lds_at(unsigned char* base, int off) {
     return reinterpret_cast<T*>(base + off);
 }
 
-// exclusive prefix sum over the workgroup (one value per thread)
+// exclusive prefix sum over the workgroup (one value per thread); tmp holds kTreeWaves ints
 __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int x = v;
@@ -235,7 +285,7 @@ __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
     if (lane == 63) tmp[wave] = x;
     __syncthreads();
     int before = 0, all = 0;
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kTreeWaves; ++w) {
         if (w < wave) before += tmp[w];
         all += tmp[w];
     }
@@ -244,11 +294,13 @@ __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
     return before + x - v;
 }
 
-__global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
+template <int RM>
+__global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const TreePlan& P = a.plan;
     const int b = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int d = a.d, k = a.k, W = a.W, budget = a.budget;
     const int kind = a.ng_kind;
     const bool dartree = a.mode == DT_MODE_DARTREE;
@@ -262,29 +314,26 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
     int* n_par = lds_at<int>(lds, P.off_n_par);
     int* n_dep = lds_at<int>(lds, P.off_n_dep);
     int* n_tidx = lds_at<int>(lds, P.off_n_tidx);
-    int* n_cctx = lds_at<int>(lds, P.off_n_cctx);
+    uint32_t* n_cmask = lds_at<uint32_t>(lds, P.off_n_cctx);   // children's continuity mask
     int* n_new = lds_at<int>(lds, P.off_n_new);
     int* n_out = lds_at<int>(lds, P.off_n_out);
     double* n_rk = lds_at<double>(lds, P.off_n_rk);
     double* n_s = lds_at<double>(lds, P.off_n_s);
-    double* c_rk = lds_at<double>(lds, P.off_c_rk);
-    double* c_s = lds_at<double>(lds, P.off_c_s);
-    uint32_t* c_tie = lds_at<uint32_t>(lds, P.off_c_tie);
-    int* c_surv = lds_at<int>(lds, P.off_c_surv);
-    double* rowmax = lds_at<double>(lds, P.off_rowmax);
     int* misc = lds_at<int>(lds, P.off_misc);
-    unsigned long long* merge = lds_at<unsigned long long>(lds, P.off_merge) + wave * kMergeKeysPerRow;
+    unsigned long long* merge = lds_at<unsigned long long>(lds, P.off_merge) +
+                                (wave < kMergeWaves ? wave : 0) * kMergeKeysPerRow;
 
     const int ctx0 = a.ctx[2 * b], ctx1 = a.ctx[2 * b + 1];
 
     // ---- 1. normalisers and top-k lists of the d positions
-    for (int i = wave; i < d; i += kWaves)
-        merge_row(a.part_m, a.part_s, a.part_keys, (int64_t)b * d + i, a.C, k, merge, lane,
-                  &s_lse[i], &s_ttok[i * k], &s_tx[i * k]);
+    if (wave < kMergeWaves)
+        for (int i = wave; i < d; i += kMergeWaves)
+            merge_row(a.part_m, a.part_s, a.part_keys, (int64_t)b * d + i, a.C, k, merge, lane,
+                      &s_lse[i], &s_ttok[i * k], &s_tx[i * k]);
     __syncthreads();
 
     // ---- 2a. continuity of every context a parent can have
-    for (int ci = tid; ci < P.n_ctx; ci += kThreads) {
+    for (int ci = tid; ci < P.n_ctx; ci += kTreeThreads) {
         int t, a2, a1;
         if (ci == 0) {
             t = 1; a2 = ctx0; a1 = ctx1;
@@ -311,23 +360,45 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
     if (dartree) {
         const int tk = (k + 15) >> 4;
         const int tiles = d * tk * tk;
-        for (int tile = wave; tile < tiles; tile += kWaves) {
+        for (int tile = wave; tile < tiles; tile += kTreeWaves) {
             const int t = 1 + tile / (tk * tk);
             const int r = tile - (t - 1) * tk * tk;
             const int ti = r / tk, tj = r - ti * tk;
             const int kp = t == 1 ? 1 : k;
             if (ti * 16 >= kp) continue;                      // wave-uniform
-            const int i = ti * 16 + (lane & 15), j = tj * 16 + (lane & 15), kk = lane >> 4;
+            const int i = ti * 16 + (lane & 15), j = tj * 16 + (lane & 15), grp = lane >> 4;
             int ptok = i < kp ? (t == 1 ? ctx1 : s_ttok[(t - 2) * k + i]) : -1;
             if (ptok >= a.V) ptok = -1;                           // out-of-range root id: no term
             const int ctok = j < k ? s_ttok[(t - 1) * k + j] : -1;
             const float* er = ptok >= 0 ? a.E + (int64_t)ptok * a.R : nullptr;
             const float* fr = ctok >= 0 ? a.F + (int64_t)ctok * a.R : nullptr;
+            // The dot product is a sum over the rank index; step q of a block of
+            // 4*per columns takes column grp*per + q from lane group grp, so each
+            // lane reads `per` contiguous floats of its row (16-byte loads).
             v4d acc = {0.0, 0.0, 0.0, 0.0};
-            for (int s = 0; s < a.R; s += 4) {
-                const double av = er ? (double)er[s + kk] : 0.0;   // A[i][kk]
-                const double bv = fr ? (double)fr[s + kk] : 0.0;   // B[kk][j]
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+            for (int r0 = 0; r0 < a.R; r0 += 64) {
+                const int per = (a.R - r0 < 64 ? a.R - r0 : 64) >> 2;
+                float ea[16], fb[16];
+                if (per == 16) {
+                    typedef float f4 __attribute__((ext_vector_type(4)));
+                    const f4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const f4 x = er ? reinterpret_cast<const f4*>(er + r0 + grp * 16)[v] : z;
+                        const f4 y = fr ? reinterpret_cast<const f4*>(fr + r0 + grp * 16)[v] : z;
+                        ea[4 * v] = x.x; ea[4 * v + 1] = x.y; ea[4 * v + 2] = x.z; ea[4 * v + 3] = x.w;
+                        fb[4 * v] = y.x; fb[4 * v + 1] = y.y; fb[4 * v + 2] = y.z; fb[4 * v + 3] = y.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        ea[q] = (er && q < per) ? er[r0 + grp * per + q] : 0.f;
+                        fb[q] = (fr && q < per) ? fr[r0 + grp * per + q] : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    if (q < per) acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ea[q], (double)fb[q], acc, 0, 0, 0);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {                          // D[lane/16 + 4q][lane%16]
@@ -336,112 +407,89 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
             }
         }
     }
-    if (tid < 4) misc[tid] = 0;
     __syncthreads();
 
-    // ---- 3. depth loop
+    // ---- 3. depth loop.  Every wave computes every candidate key into
+    //      registers (slot r*64 + lane, slot = parent_rank * k + child), ranks
+    //      the slots it owns by comparing one key (read with readlane) against
+    //      all of them and counting with ballots, and the owning lane writes the
+    //      winners.  One barrier per depth.
     int f = 1;        // frontier size (depth 0: the root)
     int fbase = 0;    // BFS index of the first frontier node
     int nb = 0;       // nodes in the candidate tree
+    const uint32_t root_mask = kind == DT_NGRAM_NONE ? 0xFFFFFFFFu : s_vmask[0];
     for (int t = 1; t <= d; ++t) {
-        int* cnt = &misc[t & 1];
-        const int m = f * k;                 // candidate slots, slot = p * k + j
+        const int m = f * k;
+        const int R = (m + 63) >> 6;
         const double lse_t = s_lse[t - 1];
-        int mine = 0;
-        for (int ci = tid; ci < m; ci += kThreads) {
-            const int p = ci / k, j = ci - p * k;
-            const float x = s_tx[(t - 1) * k + j];
-            bool ok = x != -INFINITY;
-            double prk = 0.0, ps = 0.0;
-            int cidx = 0, gp = 0;
-            if (t > 1) {
-                const int nd = fbase + p;
-                prk = n_rk[nd];
-                ps = n_s[nd];
-                cidx = n_cctx[nd];
-                gp = n_tidx[nd];
-            }
-            if (ok && kind != DT_NGRAM_NONE) ok = (s_vmask[cidx] >> j) & 1u;
-            double rk = -INFINITY, sc = -INFINITY;
-            if (ok) {
-                const double g = dartree ? s_g[((t - 1) * k + gp) * k + j] : 0.0;
-                rk = (prk + (double)x) + g;
-                sc = (ps + ((double)x - lse_t)) + g;
-                ++mine;
-            }
-            c_rk[ci] = rk;
-            c_s[ci] = sc;
-            c_tie[ci] = ((uint32_t)s_ttok[(t - 1) * k + j] << 6) | (uint32_t)p;
-        }
-        if (mine) atomicAdd(cnt, mine);
-        if (tid == 0) {
-            misc[(t + 1) & 1] = 0;
-            misc[2] = 0;
-        }
-        __syncthreads();
-        const int n = *(volatile int*)cnt;
-        if (n == 0) break;
-        const int keep = n < W ? n : W;
-
-        // candidates to rank: all slots, or, when the frontier is full and the
-        // slots are many, only those whose key reaches the smallest row maximum
-        // (the W row maxima are W candidates at or above it)
-        const bool filter = f == W && m > 128;
-        int ns = m;
-        if (filter) {
-            for (int p = tid; p < f; p += kThreads) {
-                double best = -INFINITY;
-                for (int j = 0; j < k; ++j) best = fmax(best, c_rk[p * k + j]);
-                rowmax[p] = best;
-            }
-            __syncthreads();
-            double lb = INFINITY;
-            for (int p = 0; p < f; ++p) lb = fmin(lb, rowmax[p]);
-            for (int ci = tid; ci < m; ci += kThreads) {
-                const bool in = c_rk[ci] != -INFINITY && c_rk[ci] >= lb;
-                const unsigned long long bal = __ballot(in);
-                int base = 0;
-                if (lane == 0 && bal) base = atomicAdd(&misc[2], __popcll(bal));
-                base = __shfl(base, 0);
-                if (in) c_surv[base + lanes_below(bal)] = ci;
-            }
-            __syncthreads();
-            ns = *(volatile int*)&misc[2];
-        }
-
-        // rank by counting; tpc threads share one candidate's comparisons
-        int tpc = 1;
-        while (tpc < 8 && 2 * tpc * ns <= kThreads) tpc <<= 1;
-        for (int base = 0; base < ns * tpc; base += kThreads) {
-            const int e = base + tid;
-            const int c = e / tpc, part = e - c * tpc;
-            int r = 0;
-            int slot = -1;
-            bool live = false;
-            if (c < ns) {
-                slot = filter ? c_surv[c] : c;
-                const double my = c_rk[slot];
-                const uint32_t mt = c_tie[slot];
-                live = my != -INFINITY;
-                if (live) {
-                    for (int q = part; q < ns; q += tpc) {
-                        const int o = filter ? c_surv[q] : q;
-                        r += cand_before(c_rk[o], c_tie[o], my, mt);
-                    }
+        const int tk = (t - 1) * k;
+        double krk[RM], ksc[RM];
+        uint32_t ktie[RM];
+        unsigned long long vb[RM];
+        int nvalid = 0;
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            const int slot = r * 64 + lane;
+            bool ok = false;
+            krk[r] = -INFINITY;
+            ksc[r] = -INFINITY;
+            ktie[r] = 0xFFFFFFFFu;
+            if (r < R && slot < m) {
+                const int p = slot / k, j = slot - p * k;
+                const float x = s_tx[tk + j];
+                uint32_t cm = root_mask;
+                double prk = 0.0, ps = 0.0;
+                int gp = 0;
+                if (t > 1) {
+                    const int nd = fbase + p;
+                    cm = n_cmask[nd];
+                    prk = n_rk[nd];
+                    ps = n_s[nd];
+                    gp = n_tidx[nd];
+                }
+                ok = x != -INFINITY && ((cm >> j) & 1u);
+                if (ok) {
+                    const double g = dartree ? s_g[(tk + gp) * k + j] : 0.0;
+                    krk[r] = (prk + (double)x) + g;
+                    ksc[r] = (ps + ((double)x - lse_t)) + g;
+                    ktie[r] = ((uint32_t)s_ttok[tk + j] << 6) | (uint32_t)p;
                 }
             }
-            for (int off = 1; off < tpc; off <<= 1) r += __shfl_xor(r, off);
-            if (live && part == 0 && r < keep) {
-                const int p = slot / k, j = slot - p * k;
-                const int nd = nb + r;
-                n_tok[nd] = s_ttok[(t - 1) * k + j];
-                n_par[nd] = t == 1 ? -1 : fbase + p;
-                n_dep[nd] = t;
-                n_tidx[nd] = j;
-                const int pj = t == 1 ? 0 : n_tidx[fbase + p];
-                n_cctx[nd] = t < d ? ctx_index(kind, k, t + 1, pj, j) : 0;
-                n_rk[nd] = c_rk[slot];
-                n_s[nd] = c_s[slot];
+            vb[r] = __ballot(ok);
+            nvalid += __popcll(vb[r]);
+        }
+        if (nvalid == 0) break;                 // identical in every wave
+        const int keep = nvalid < W ? nvalid : W;
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            if (r >= R) break;
+            for (int l = wave; l < 64; l += kTreeWaves) {
+                if (!((vb[r] >> l) & 1ull)) continue;
+                const double my = readlane_d(krk[r], l);
+                const uint32_t mt = (uint32_t)__builtin_amdgcn_readlane((int)ktie[r], l);
+                int rank = 0;
+#pragma unroll
+                for (int r2 = 0; r2 < RM; ++r2) {
+                    if (r2 >= R) break;
+                    rank += __popcll(__ballot(cand_before(krk[r2], ktie[r2], my, mt)));
+                }
+                if (rank < keep && lane == l) {
+                    const int slot = r * 64 + l;
+                    const int p = slot / k, j = slot - p * k;
+                    const int nd = nb + rank;
+                    n_tok[nd] = s_ttok[tk + j];
+                    n_par[nd] = t == 1 ? -1 : fbase + p;
+                    n_dep[nd] = t;
+                    n_tidx[nd] = j;
+                    n_rk[nd] = krk[r];
+                    n_s[nd] = ksc[r];
+                    uint32_t cm = 0xFFFFFFFFu;
+                    if (kind != DT_NGRAM_NONE && t < d) {
+                        const int pj = t == 1 ? 0 : n_tidx[fbase + p];
+                        cm = s_vmask[ctx_index(kind, k, t + 1, pj, j)];
+                    }
+                    n_cmask[nd] = cm;
+                }
             }
         }
         __syncthreads();
@@ -453,14 +501,14 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
     // ---- 4. verification budget
     int n_sel = nb;
     if (nb <= budget) {
-        for (int i = tid; i < nb; i += kThreads) {
+        for (int i = tid; i < nb; i += kTreeThreads) {
             n_new[i] = i;
             n_out[i] = i;
         }
         __syncthreads();
     } else if (!dartree) {
         // parent-closed top-budget by (S desc, BFS index asc)
-        const int per = (nb + kThreads - 1) / kThreads;
+        const int per = (nb + kTreeThreads - 1) / kTreeThreads;
         int flags = 0, cntl = 0;
         for (int q = 0; q < per; ++q) {
             const int i = tid * per + q;
@@ -475,7 +523,7 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
             }
         }
         int total;
-        int pos = block_exclusive_scan(cntl, misc + 4, &total);
+        int pos = block_exclusive_scan(cntl, misc + 16, &total);
         for (int q = 0; q < per; ++q) {
             const int i = tid * per + q;
             if (i < nb) {
@@ -492,7 +540,7 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
         __syncthreads();
     } else {
         // best-first, literally: take the best available node budget times
-        for (int i = tid; i < nb; i += kThreads) n_new[i] = (n_par[i] < 0) ? -2 : -3;  // -2 available, -3 waiting
+        for (int i = tid; i < nb; i += kTreeThreads) n_new[i] = (n_par[i] < 0) ? -2 : -3;  // -2 available, -3 waiting
         __syncthreads();
         if (wave == 0) {
             for (int step = 0; step < budget; ++step) {
@@ -523,14 +571,14 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
         }
         __syncthreads();
         // taken nodes keep BFS order
-        const int per = (nb + kThreads - 1) / kThreads;
+        const int per = (nb + kTreeThreads - 1) / kTreeThreads;
         int cntl = 0;
         for (int q = 0; q < per; ++q) {
             const int i = tid * per + q;
             if (i < nb && n_new[i] == -1) ++cntl;
         }
         int total;
-        int pos = block_exclusive_scan(cntl, misc + 4, &total);
+        int pos = block_exclusive_scan(cntl, misc + 16, &total);
         __syncthreads();
         for (int q = 0; q < per; ++q) {
             const int i = tid * per + q;
@@ -550,7 +598,7 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
 
     // ---- 5. outputs in BFS order, parents remapped, ancestor mask
     const int64_t ob = (int64_t)b * budget;
-    for (int o = tid; o < budget; o += kThreads) {
+    for (int o = tid; o < budget; o += kTreeThreads) {
         if (o < n_sel) {
             const int i = n_out[o];
             a.tokens[ob + o] = n_tok[i];
@@ -565,7 +613,7 @@ __global__ void __launch_bounds__(kThreads) tree_kernel(TreeArgs a) {
         }
     }
     const int words = a.mask_words;
-    for (int e = tid; e < budget * words; e += kThreads) {
+    for (int e = tid; e < budget * words; e += kTreeThreads) {
         const int o = e / words, w = e - o * words;
         uint32_t bits = 0;
         if (o < n_sel) {
@@ -601,7 +649,13 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
 
 hipError_t launch_tree(const TreeArgs& a, hipStream_t stream) {
     if (a.B <= 0) return hipSuccess;
-    hipLaunchKernelGGL(tree_kernel, dim3((unsigned)a.B), dim3(kThreads), (size_t)a.plan.total, stream, a);
+    const int m = a.W * a.k;
+    if (m <= 128)
+        hipLaunchKernelGGL(tree_kernel<2>, dim3((unsigned)a.B), dim3(kTreeThreads), (size_t)a.plan.total, stream, a);
+    else if (m <= 256)
+        hipLaunchKernelGGL(tree_kernel<4>, dim3((unsigned)a.B), dim3(kTreeThreads), (size_t)a.plan.total, stream, a);
+    else
+        hipLaunchKernelGGL(tree_kernel<16>, dim3((unsigned)a.B), dim3(kTreeThreads), (size_t)a.plan.total, stream, a);
     return hipGetLastError();
 }
 
