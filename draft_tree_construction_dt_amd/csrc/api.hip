@@ -23,7 +23,7 @@ SweepPlan plan_sweep(const dt_params* p) {
         const int64_t target = 512;
         int64_t c = s.rows >= target ? 1 : ceil_div(target, s.rows > 0 ? s.rows : 1);
         const int64_t by_len = V / 4096 > 1 ? V / 4096 : 1;
-        const int64_t by_merge = kMergeKeysPerRow / p->k;
+        const int64_t by_merge = kMergeKeysPerRow / (p->k * kWaves);
         if (c > by_len) c = by_len;
         if (c > by_merge) c = by_merge;
         C = (int)(c < 1 ? 1 : c);
@@ -36,7 +36,7 @@ SweepPlan plan_sweep(const dt_params* p) {
 
 WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s) {
     WorkspacePlan w{};
-    const int64_t n = s.rows * s.C;
+    const int64_t n = s.rows * s.C * kWaves;     // one partial list per sweep wave
     w.off_m = 0;
     w.off_s = (size_t)round_up(n * 4, 256);
     w.off_keys = (size_t)round_up((int64_t)w.off_s + n * 8, 256);
@@ -67,6 +67,8 @@ TreePlan plan_tree(const dt_params* p, int kind) {
     P.off_ctxbase = 0;
     P.off_vmask = take(P.n_ctx * 4, 4);
     P.off_misc = take(kMiscInts * 4, 4);
+    P.off_sv_key = take(P.max_cand * 16, 16);
+    P.off_sv_s = take(P.max_cand * 8, 8);
     // node arrays; the per-wave merge scratch of step 1 reuses this space
     const int region = (int)round_up(off, 16);
     off = region;
@@ -102,7 +104,7 @@ static dt_status check_shape(const dt_params* p) {
         p->W * p->k > kMaxCandidates || p->V >= kMaxV)
         return DT_ERR_UNSUPPORTED;
     const SweepPlan s = plan_sweep(p);
-    if ((int64_t)s.C * p->k > kMergeKeysPerRow) return DT_ERR_UNSUPPORTED;
+    if ((int64_t)s.C * kWaves * p->k > kMergeKeysPerRow) return DT_ERR_UNSUPPORTED;
     return DT_OK;
 }
 
@@ -210,7 +212,7 @@ extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngr
     ta.W = p->W;
     ta.budget = p->budget;
     ta.mode = p->mode;
-    ta.C = s.C;
+    ta.C = s.C * kWaves;                          // partial lists per row
     ta.R = p->R;
     ta.mask_words = (p->budget + 31) / 32;
     ta.ctx = p->ctx;
@@ -254,7 +256,7 @@ extern "C" dt_status dt_position_topk(const void* logits, const dt_params* p, do
     char* ws = (char*)p->workspace;
     MergeArgs ma{};
     ma.rows = (int)s.rows;
-    ma.C = s.C;
+    ma.C = s.C * kWaves;
     ma.k = p->k;
     ma.part_m = (const float*)(ws + w.off_m);
     ma.part_s = (const double*)(ws + w.off_s);

@@ -22,7 +22,7 @@ constexpr int kTreeWaves = kTreeThreads / 64;
 constexpr int kMergeWaves = 8;         // tree-kernel waves that merge the sweep partials
 constexpr int kMiscInts = 32;          // tree-kernel counters (0..3) and scan scratch (16..31)
 constexpr int kTreeLdsLimit = 64 * 1024;
-constexpr int kMergeKeysPerRow = 256;  // C * k bound: per-wave merge scratch in the tree kernel
+constexpr int kMergeKeysPerRow = 256;  // C * 4 * k bound: per-wave merge scratch in the tree kernel
 constexpr int kSweepVecsPerThread = 4; // 16-byte vectors each thread holds per batch
 constexpr int kSweepCap = 128;         // per-wave candidate buffer of the sweep
 
@@ -52,10 +52,10 @@ struct SweepPlan {
     int64_t rows;
 };
 
-// Workspace: per (row, chunk) partial results of the sweep.
-//   part_m    float  [rows][C]      running max of the chunk
-//   part_s    double [rows][C]      sum exp(x - part_m) over the chunk
-//   part_keys uint64 [rows][C][k]   the chunk's top-k keys, descending; 0 pads
+// Workspace: per (row, chunk, sweep wave) partial results of the sweep.
+//   part_m    float  [rows][C*4]      running max of the wave's elements
+//   part_s    double [rows][C*4]      sum exp(x - part_m) over them
+//   part_keys uint64 [rows][C*4][k]   their top-k keys, descending; 0 pads
 struct WorkspacePlan {
     size_t off_m, off_s, off_keys, total;
 };
@@ -75,6 +75,8 @@ struct TreePlan {
     int off_n_tok, off_n_par, off_n_dep, off_n_tidx, off_n_cctx, off_n_new, off_n_out;
     int off_n_rk, off_n_s;
     int off_merge;      // uint64 [kMergeWaves][kMergeKeysPerRow] (aliases the node arrays)
+    int off_sv_key;     // 16-byte survivor keys [W*k] of the depth loop
+    int off_sv_s;       // double [W*k] their cumulative scores
     int off_misc;       // int counters
     int total;
 };

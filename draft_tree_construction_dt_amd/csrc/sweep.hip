@@ -5,7 +5,9 @@
 // tokens.  This pass reads every logit exactly once and carries nearly all
 // of the path's HBM traffic.
 //
-// Layout: a 256-thread workgroup owns one chunk of one row.  Each thread
+// Layout: a 256-thread workgroup owns one chunk of one row; each of its four
+// waves streams a quarter of every batch and emits its own partial list (no
+// barriers, no shared state between waves).  Each thread
 // keeps kSweepVecsPerThread 16-byte vectors (8 bf16 or 4 fp32) per batch, the
 // 64 lanes of a wave reading 1 KiB contiguous per load; loads are
 // non-temporal (streamed once) and the next batch is loaded before the
@@ -21,6 +23,9 @@ namespace dt {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+extern "C" __device__ float __ockl_wfred_max_f32(float);      // DPP wavefront reductions (ROCm ockl)
+extern "C" __device__ double __ockl_wfred_add_f64(double);
 constexpr int U = kSweepVecsPerThread;
 typedef uint32_t vec4 __attribute__((ext_vector_type(4)));
 constexpr int CAP = kSweepCap;
@@ -154,17 +159,24 @@ __device__ __forceinline__ void unpack(const vec4& r, float* out) {
 }
 
 template <bool BF16>
+__device__ __forceinline__ void load_batch(vec4 (&r)[U], const vec4* vbase, int64_t q, int64_t v_hi) {
+    constexpr uint32_t NEG = BF16 ? 0xFF80FF80u : 0xFF800000u;   // -inf patterns
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t qu = q + (int64_t)u * kThreads;
+        r[u] = qu < v_hi ? __builtin_nontemporal_load(vbase + qu) : vec4{NEG, NEG, NEG, NEG};
+    }
+}
+
+template <bool BF16>
 __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
     constexpr int EPV = BF16 ? 8 : 4;
     constexpr int NE = U * EPV;
-    constexpr uint32_t NEG = BF16 ? 0xFF80FF80u : 0xFF800000u;   // -inf patterns
 
     __shared__ unsigned long long s_buf[kWaves][CAP];
-    __shared__ float s_wm[kWaves];
-    __shared__ double s_ws[kWaves];
-    __shared__ int s_wcnt[kWaves];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t row = blockIdx.x / a.C;
     const int chunk = blockIdx.x - (int)(row * a.C);
     const int k = a.k;
@@ -196,55 +208,33 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
     st.thid = 0xFFFFFFFFu;
     st.fresh = true;
 
-    // ---- full batches, software pipelined: load batch i+1 before reducing batch i
+    // ---- batches of kThreads*U vectors, software pipelined: the next batch
+    //      (the last one guarded) is loaded before the current one is reduced
     const int64_t per_batch = (int64_t)kThreads * U;
     const int64_t nvec = v_hi - v_lo;
-    const int64_t nfull = nvec / per_batch;
-    if (nfull > 0) {
+    const int64_t nbat = (nvec + per_batch - 1) / per_batch;
+    if (nbat > 0) {
         vec4 cur[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            cur[u] = __builtin_nontemporal_load(vbase + v_lo + (int64_t)u * kThreads + tid);
-        for (int64_t bi = 0; bi < nfull; ++bi) {
+        load_batch<BF16>(cur, vbase, v_lo + tid, v_hi);
+        for (int64_t bi = 0; bi < nbat; ++bi) {
             const int64_t q0 = v_lo + bi * per_batch + tid;
             vec4 nxt[U];
-            if (bi + 1 < nfull) {
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    nxt[u] = __builtin_nontemporal_load(vbase + q0 + per_batch + (int64_t)u * kThreads);
-            }
-            float xs[NE];
-            int id0[U];
-            bool vok[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                unpack<BF16>(cur[u], xs + u * EPV);
-                id0[u] = (int)((q0 + (int64_t)u * kThreads) * EPV - row0);
-                vok[u] = true;
-            }
-            consume<NE, EPV>(xs, id0, vok, st, buf, k, trig, lane);
-            if (bi + 1 < nfull) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-            }
-        }
-    }
-    // ---- the remaining vectors (fewer than one batch), guarded
-    {
-        const int64_t q0 = v_lo + nfull * per_batch + tid;
-        if (nfull * per_batch < nvec) {
+            if (bi + 1 < nbat) load_batch<BF16>(nxt, vbase, q0 + per_batch, v_hi);
             float xs[NE];
             int id0[U];
             bool vok[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t q = q0 + (int64_t)u * kThreads;
-                vok[u] = q < v_hi;
-                const vec4 r = vok[u] ? __builtin_nontemporal_load(vbase + q) : vec4{NEG, NEG, NEG, NEG};
-                unpack<BF16>(r, xs + u * EPV);
+                unpack<BF16>(cur[u], xs + u * EPV);
                 id0[u] = (int)(q * EPV - row0);
+                vok[u] = q < v_hi;
             }
             consume<NE, EPV>(xs, id0, vok, st, buf, k, trig, lane);
+            if (bi + 1 < nbat) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+            }
         }
     }
     // ---- elements outside the aligned vectors (row ends that are not 16-byte aligned)
@@ -270,55 +260,18 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
         }
     }
 
-    // ---- this wave's top-k, sorted
+    // ---- this wave's partial: its top-k sorted, and (max, sum exp(x - max));
+    //      every wave writes its own list, so waves never wait for each other
     wave_select(buf, st, k, lane);
-
-    // ---- wave reduction of the softmax state
-    float M = st.m;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    double sl = (st.m == -INFINITY) ? 0.0 : st.s * (double)__builtin_amdgcn_exp2f((st.m - M) * kLog2e);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sl += __shfl_xor(sl, off);
+    const float M = __ockl_wfred_max_f32(st.m);
+    const double sl = (st.m == -INFINITY) ? 0.0 : st.s * (double)__builtin_amdgcn_exp2f((st.m - M) * kLog2e);
+    const double S = __ockl_wfred_add_f64(sl);
+    const int64_t list = (row * a.C + chunk) * kWaves + wave;
+    unsigned long long* out = a.part_keys + list * k;
+    if (lane < k) out[lane] = lane < st.cnt ? buf[lane] : 0ull;
     if (lane == 0) {
-        s_wm[wave] = M;
-        s_ws[wave] = sl;
-        s_wcnt[wave] = st.cnt;
-    }
-    __syncthreads();
-
-    // ---- workgroup merge (wave 0): top-k of the four wave lists, and (m, s)
-    if (wave == 0) {
-        const int n = kWaves * k;                 // entry e: wave e / k, slot e % k
-        unsigned long long ka = 0ull, kb = 0ull;
-        {
-            const int e = lane, w = e / k, i = e - w * k;
-            if (e < n && i < s_wcnt[w]) ka = s_buf[w][i];
-            const int e2 = lane + 64, w2 = e2 / k, i2 = e2 - w2 * k;
-            if (e2 < n && i2 < s_wcnt[w2]) kb = s_buf[w2][i2];
-        }
-        int ra = 0, rb = 0;
-        for (int j = 0; j < n; ++j) {
-            const int w = j / k, i = j - w * k;
-            const unsigned long long v = i < s_wcnt[w] ? s_buf[w][i] : 0ull;
-            ra += v > ka;
-            rb += v > kb;
-        }
-        const int total = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
-        unsigned long long* out = a.part_keys + (row * a.C + chunk) * (int64_t)k;
-        if (ka != 0ull && ra < k) out[ra] = ka;
-        if (kb != 0ull && rb < k) out[rb] = kb;
-        if (lane < k && lane >= total) out[lane] = 0ull;
-        if (lane == 0) {
-            float Mw = s_wm[0];
-            for (int w = 1; w < kWaves; ++w) Mw = fmaxf(Mw, s_wm[w]);
-            double S = 0.0;
-            if (Mw != -INFINITY)
-                for (int w = 0; w < kWaves; ++w)
-                    if (s_wm[w] != -INFINITY) S += s_ws[w] * exp((double)s_wm[w] - (double)Mw);
-            a.part_m[row * a.C + chunk] = Mw;
-            a.part_s[row * a.C + chunk] = S;
-        }
+        a.part_m[list] = M;
+        a.part_s[list] = S;
     }
 }
 

@@ -31,6 +31,7 @@ namespace dt {
 namespace {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
+extern "C" __device__ double __ockl_wfred_min_f64(double);
 constexpr unsigned long long kEmptyKey = 0xFFFFFFFFFFFFFFFFull;
 
 __device__ __forceinline__ float key_value(unsigned long long key) {
@@ -41,6 +42,18 @@ __device__ __forceinline__ uint32_t key_id(unsigned long long key) { return ~(ui
 __device__ __forceinline__ int lanes_below(unsigned long long mask) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+extern "C" __device__ float __ockl_wfred_max_f32(float);      // DPP wavefront reductions (ROCm ockl)
+extern "C" __device__ double __ockl_wfred_add_f64(double);
+extern "C" __device__ unsigned long long __ockl_wfred_max_u64(unsigned long long);
+extern "C" __device__ unsigned long long __ockl_wfred_min_u64(unsigned long long);
+extern "C" __device__ int __ockl_wfred_add_i32(int);
+
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
+    const int lo = __builtin_amdgcn_readlane((int)(v & 0xFFFFFFFFull), l);
+    const int hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+    return ((unsigned long long)(unsigned int)hi << 32) | (unsigned int)lo;
 }
 
 __device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
@@ -70,60 +83,98 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 }
 
 // ---------------------------------------------------------------------------
-// 1. one wave merges the C partials of one row
+// 1. one wave merges the L partial lists of one row
 // ---------------------------------------------------------------------------
 __device__ void merge_row(const float* __restrict__ part_m, const double* __restrict__ part_s,
-                          const unsigned long long* __restrict__ part_keys, int64_t row, int C, int k,
+                          const unsigned long long* __restrict__ part_keys, int64_t row, int L, int k,
                           unsigned long long* scratch, int lane, double* lse_out, int* tok_out,
                           float* val_out) {
-    const float* pm = part_m + row * C;
-    const double* ps = part_s + row * C;
-    float mc = -INFINITY;
-    for (int c = lane; c < C; c += 64) mc = fmaxf(mc, pm[c]);
-    const float M = wave_max_f(mc);
+    const float* pm = part_m + row * L;
+    const double* ps = part_s + row * L;
+    const unsigned long long* keys = part_keys + row * (int64_t)L * k;
+    const int n = L * k;
+    // all loads of the row are independent: issue them together
+    float mc[4];
+    double sc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = lane + 64 * q;
+        mc[q] = c < L ? pm[c] : -INFINITY;
+        sc[q] = c < L ? ps[c] : 0.0;
+    }
+    unsigned long long kv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        kv[q] = e < n ? keys[e] : 0ull;
+    }
+
+    // normaliser: max and rescaled sum over the lists, log in fp64
+    const float M = __ockl_wfred_max_f32(fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3])));
     double sum = 0.0;
-    if (M != -INFINITY)
-        for (int c = lane; c < C; c += 64) {
-            const float m = pm[c];
-            if (m != -INFINITY) sum += ps[c] * exp((double)m - (double)M);
-        }
-    sum = wave_sum_d(sum);
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (mc[q] != -INFINITY) sum += sc[q] * (double)__builtin_amdgcn_exp2f((mc[q] - M) * 1.4426950408889634f);
+    }
+    sum = __ockl_wfred_add_f64(sum);
     if (lane == 0) {
         // the true normaliser is >= the row max; clamp the rounding of a sum
         // whose largest term is 1 so that every log-probability stays <= 0
-        double l = log(sum);
+        const double l = log(sum);
         *lse_out = (M == -INFINITY) ? -INFINITY : (double)M + (l > 0.0 ? l : 0.0);
     }
 
-    // top-k: every chunk list is sorted; the k-th key of any full list is a
-    // lower bound for the row's k-th key, so only keys >= the largest such
-    // bound can be in the row's top-k
-    const unsigned long long* keys = part_keys + row * (int64_t)C * k;
-    const int n = C * k;
-    unsigned long long th = 0ull;
-    for (int c = lane; c < C; c += 64) {
-        const unsigned long long v = keys[(int64_t)c * k + k - 1];
-        th = v > th ? v : th;
+    // top-k.  Lower bounds for the row's k-th key, both from k distinct keys:
+    // the k-th key of any full list, and the q-th key of every list holding
+    // q = ceil(k/L) keys when there are enough such lists.
+    const int q = (k + L - 1) / L;
+    unsigned long long bk = 0ull, bq = ~0ull;
+    int nq = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int e = lane + 64 * r;
+        if (e < n) {
+            const int i = e % k;
+            if (i == k - 1) bk = kv[r] > bk ? kv[r] : bk;
+            if (i == q - 1 && kv[r] != 0ull) {
+                bq = kv[r] < bq ? kv[r] : bq;
+                ++nq;
+            }
+        }
     }
-    th = wave_max_u64(th);
+    bk = __ockl_wfred_max_u64(bk);
+    bq = __ockl_wfred_min_u64(bq);
+    nq = __ockl_wfred_add_i32(nq);
+    unsigned long long th = bk;
+    if (nq * q >= k && bq > th) th = bq;
     int ns = 0;
-    for (int base = 0; base < n; base += 64) {
-        const int e = base + lane;
-        const unsigned long long v = e < n ? keys[e] : 0ull;
-        const bool keep = v != 0ull && v >= th;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool keep = kv[r] != 0ull && kv[r] >= th;
         const unsigned long long bal = __ballot(keep);
-        if (keep) scratch[ns + lanes_below(bal)] = v;
+        if (keep) scratch[ns + lanes_below(bal)] = kv[r];
         ns += __popcll(bal);
     }
     __builtin_amdgcn_wave_barrier();
-    for (int base = 0; base < ns; base += 64) {
-        const int e = base + lane;
-        const unsigned long long v = e < ns ? scratch[e] : 0ull;
-        int r = 0;
-        for (int j = 0; j < ns; ++j) r += scratch[j] > v;
-        if (e < ns && r < k) {
-            tok_out[r] = (int)key_id(v);
-            val_out[r] = key_value(v);
+    // rank: lane e holds survivor e (blocks of 64) and streams past all of
+    // them (keys are unique)
+    for (int e0 = 0; e0 < ns; e0 += 64) {
+        const int e = e0 + lane;
+        const unsigned long long v = e < ns ? scratch[e] : ~0ull;
+        int rank = 0;
+        int j = 0;
+        for (; j + 8 <= ns; j += 8) {
+            unsigned long long o[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o[u] = scratch[j + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rank += o[u] > v;
+        }
+        for (; j < ns; ++j) rank += scratch[j] > v;
+        if (e < ns && rank < k) {
+            tok_out[rank] = (int)key_id(v);
+            val_out[rank] = key_value(v);
         }
     }
     __builtin_amdgcn_wave_barrier();
@@ -179,6 +230,22 @@ __device__ __forceinline__ long long find_slot(const TreeArgs& a, unsigned long 
     return -1;
 }
 
+// Up to 16 successor ids of a row (-1 beyond n): four 16-byte loads when the
+// row is 16-byte aligned and holds whole vectors, scalar loads otherwise.
+__device__ __forceinline__ void load_row16(int (&r)[16], const int* p, int n) {
+    typedef int i4 __attribute__((ext_vector_type(4)));
+    if (n >= 16 && ((uintptr_t)p & 15u) == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const i4 x = reinterpret_cast<const i4*>(p)[v];
+            r[4 * v] = x.x; r[4 * v + 1] = x.y; r[4 * v + 2] = x.z; r[4 * v + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) r[u] = u < n ? p[u] : -1;
+    }
+}
+
 // Bit j set iff child T_{t-1}[j] (finite logit) is admitted after (a2, a1).
 __device__ uint32_t admitted_children(const TreeArgs& a, int a2, int a1, const int* ch, const float* cx) {
     const int k = a.k;
@@ -215,14 +282,23 @@ __device__ uint32_t admitted_children(const TreeArgs& a, int a2, int a1, const i
         }
     } else if (a.ng_kind == DT_NGRAM_HASH_TRIGRAM) {
         const unsigned long long key = ((unsigned long long)(uint32_t)a2 << 32) | (uint32_t)a1;
+        // the successor row of the home slot is read while the key group is
+        // probed: a present key usually sits in its home slot
+        const long long home = (long long)(mix64(key) & ((unsigned long long)a.cap - 1ull));
+        int spec[16];
+        load_row16(spec, a.succ + home * a.S, a.S);
         const long long slot = find_slot(a, key);
         if (slot < 0) return 0;
         const int* succ = a.succ + slot * a.S;
         const bool membership = a.min_logp == -INFINITY || a.hash_logp == nullptr;
         for (int s0 = 0; s0 < a.S; s0 += 16) {
             int reg[16];
+            if (slot == home && s0 == 0) {
 #pragma unroll
-            for (int u = 0; u < 16; ++u) reg[u] = s0 + u < a.S ? succ[s0 + u] : -1;
+                for (int u = 0; u < 16; ++u) reg[u] = spec[u];
+            } else {
+                load_row16(reg, succ + s0, a.S - s0);
+            }
             for (int j = 0; j < k; ++j) {
                 const int c = ch[j];
                 int hs = -1;
@@ -267,6 +343,13 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
     const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
     return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
+
+// a ranked candidate of the depth loop: key (Rk, tie) and its slot
+struct __align__(16) SurvKey {
+    double rk;
+    uint32_t tie;
+    uint32_t slot;
+};
 
 template <typename T>
 __device__ __forceinline__ T* lds_at(unsigned char* base, int off) {
@@ -315,6 +398,8 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     int* n_dep = lds_at<int>(lds, P.off_n_dep);
     int* n_tidx = lds_at<int>(lds, P.off_n_tidx);
     uint32_t* n_cmask = lds_at<uint32_t>(lds, P.off_n_cctx);   // children's continuity mask
+    SurvKey* sv_key = lds_at<SurvKey>(lds, P.off_sv_key);
+    double* sv_s = lds_at<double>(lds, P.off_sv_s);
     int* n_new = lds_at<int>(lds, P.off_n_new);
     int* n_out = lds_at<int>(lds, P.off_n_out);
     double* n_rk = lds_at<double>(lds, P.off_n_rk);
@@ -409,80 +494,114 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     }
     __syncthreads();
 
-    // ---- 3. depth loop.  Every wave computes every candidate key into
-    //      registers (slot r*64 + lane, slot = parent_rank * k + child), ranks
-    //      the slots it owns by comparing one key (read with readlane) against
-    //      all of them and counting with ballots, and the owning lane writes the
-    //      winners.  One barrier per depth.
-    int f = 1;        // frontier size (depth 0: the root)
-    int fbase = 0;    // BFS index of the first frontier node
+    // ---- 3. depth loop, run by wave 0 alone (wave-synchronous, no barriers).
+    //      Candidate keys go to registers (slot r*64 + lane, slot =
+    //      parent_rank * k + child).  With a full frontier only candidates whose
+    //      key reaches the smallest "first valid child" key of the W rows can be
+    //      among the top W (those W candidates are distinct); the survivors are
+    //      packed into LDS and every lane ranks its own survivor by streaming
+    //      all of them, so the winners are written in parallel.
     int nb = 0;       // nodes in the candidate tree
-    const uint32_t root_mask = kind == DT_NGRAM_NONE ? 0xFFFFFFFFu : s_vmask[0];
-    for (int t = 1; t <= d; ++t) {
-        const int m = f * k;
-        const int R = (m + 63) >> 6;
-        const double lse_t = s_lse[t - 1];
-        const int tk = (t - 1) * k;
-        double krk[RM], ksc[RM];
-        uint32_t ktie[RM];
-        unsigned long long vb[RM];
-        int nvalid = 0;
+    if (wave == 0) {
+        int f = 1;        // frontier size (depth 0: the root)
+        int fbase = 0;    // BFS index of the first frontier node
+        const uint32_t root_mask = kind == DT_NGRAM_NONE ? 0xFFFFFFFFu : s_vmask[0];
+        const float inv_k = 1.0f / (float)k;
+        for (int t = 1; t <= d; ++t) {
+            const int tk = (t - 1) * k;
+            const int m = f * k;
+            const int R = (m + 63) >> 6;
+            const double lse_t = s_lse[t - 1];
+            const uint32_t live =
+                (uint32_t)__ballot(lane < k && s_tx[tk + (lane < k ? lane : 0)] != -INFINITY);
+            double krk[RM], ksc[RM];
+            uint32_t ktie[RM];
+            bool kok[RM];
+            int nvalid = 0, nfirst = 0;
+            double firstmin = INFINITY;
 #pragma unroll
-        for (int r = 0; r < RM; ++r) {
-            const int slot = r * 64 + lane;
-            bool ok = false;
-            krk[r] = -INFINITY;
-            ksc[r] = -INFINITY;
-            ktie[r] = 0xFFFFFFFFu;
-            if (r < R && slot < m) {
-                const int p = slot / k, j = slot - p * k;
-                const float x = s_tx[tk + j];
-                uint32_t cm = root_mask;
-                double prk = 0.0, ps = 0.0;
-                int gp = 0;
-                if (t > 1) {
-                    const int nd = fbase + p;
-                    cm = n_cmask[nd];
-                    prk = n_rk[nd];
-                    ps = n_s[nd];
-                    gp = n_tidx[nd];
+            for (int r = 0; r < RM; ++r) {
+                const int slot = r * 64 + lane;
+                bool ok = false, first = false;
+                krk[r] = -INFINITY;
+                ksc[r] = -INFINITY;
+                ktie[r] = 0xFFFFFFFFu;
+                if (r < R && slot < m) {
+                    const int p = (int)(((float)slot + 0.5f) * inv_k);   // exact: slot < 2^11
+                    const int j = slot - p * k;
+                    const float x = s_tx[tk + j];
+                    uint32_t cm = root_mask;
+                    double prk = 0.0, ps = 0.0;
+                    int gp = 0;
+                    if (t > 1) {
+                        const int nd = fbase + p;
+                        cm = n_cmask[nd];
+                        prk = n_rk[nd];
+                        ps = n_s[nd];
+                        gp = n_tidx[nd];
+                    }
+                    const uint32_t rowv = cm & live;
+                    ok = (rowv >> j) & 1u;
+                    first = ok && j == __builtin_ctz(rowv);
+                    if (ok) {
+                        const double g = dartree ? s_g[(tk + gp) * k + j] : 0.0;
+                        krk[r] = (prk + (double)x) + g;
+                        ksc[r] = (ps + ((double)x - lse_t)) + g;
+                        ktie[r] = ((uint32_t)s_ttok[tk + j] << 6) | (uint32_t)p;
+                        if (first) firstmin = fmin(firstmin, krk[r]);
+                    }
                 }
-                ok = x != -INFINITY && ((cm >> j) & 1u);
-                if (ok) {
-                    const double g = dartree ? s_g[(tk + gp) * k + j] : 0.0;
-                    krk[r] = (prk + (double)x) + g;
-                    ksc[r] = (ps + ((double)x - lse_t)) + g;
-                    ktie[r] = ((uint32_t)s_ttok[tk + j] << 6) | (uint32_t)p;
-                }
+                kok[r] = ok;
+                nvalid += __popcll(__ballot(ok));
+                nfirst += __popcll(__ballot(first));
             }
-            vb[r] = __ballot(ok);
-            nvalid += __popcll(vb[r]);
-        }
-        if (nvalid == 0) break;                 // identical in every wave
-        const int keep = nvalid < W ? nvalid : W;
+            if (nvalid == 0) break;
+            const int keep = nvalid < W ? nvalid : W;
+            const double lb = nfirst >= W ? __ockl_wfred_min_f64(firstmin) : -INFINITY;
+            // pack the survivors
+            int ns = 0;
 #pragma unroll
-        for (int r = 0; r < RM; ++r) {
-            if (r >= R) break;
-            for (int l = wave; l < 64; l += kTreeWaves) {
-                if (!((vb[r] >> l) & 1ull)) continue;
-                const double my = readlane_d(krk[r], l);
-                const uint32_t mt = (uint32_t)__builtin_amdgcn_readlane((int)ktie[r], l);
-                int rank = 0;
-#pragma unroll
-                for (int r2 = 0; r2 < RM; ++r2) {
-                    if (r2 >= R) break;
-                    rank += __popcll(__ballot(cand_before(krk[r2], ktie[r2], my, mt)));
+            for (int r = 0; r < RM; ++r) {
+                const bool in = kok[r] && krk[r] >= lb;
+                const unsigned long long bal = __ballot(in);
+                if (in) {
+                    const int e = ns + lanes_below(bal);
+                    sv_key[e] = SurvKey{krk[r], ktie[r], (uint32_t)(r * 64 + lane)};
+                    sv_s[e] = ksc[r];
                 }
-                if (rank < keep && lane == l) {
-                    const int slot = r * 64 + l;
-                    const int p = slot / k, j = slot - p * k;
+                ns += __popcll(bal);
+            }
+            __builtin_amdgcn_wave_barrier();
+            // rank: lane e holds survivor e (blocks of 64); all others stream past it
+            for (int e0 = 0; e0 < ns; e0 += 64) {
+                const int e = e0 + lane;
+                SurvKey me{-INFINITY, 0xFFFFFFFFu, 0u};
+                if (e < ns) me = sv_key[e];
+                int rank = 0;
+                int q = 0;
+                for (; q + 8 <= ns; q += 8) {            // eight independent LDS reads per step
+                    SurvKey o[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) o[u] = sv_key[q + u];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        rank += (o[u].rk > me.rk) | ((o[u].rk == me.rk) & (o[u].tie < me.tie));
+                }
+                for (; q < ns; ++q) {
+                    const SurvKey o = sv_key[q];
+                    rank += (o.rk > me.rk) | ((o.rk == me.rk) & (o.tie < me.tie));
+                }
+                if (e < ns && rank < keep) {
+                    const int slot = (int)me.slot;
+                    const int p = (int)(((float)slot + 0.5f) * inv_k);
+                    const int j = slot - p * k;
                     const int nd = nb + rank;
                     n_tok[nd] = s_ttok[tk + j];
                     n_par[nd] = t == 1 ? -1 : fbase + p;
                     n_dep[nd] = t;
                     n_tidx[nd] = j;
-                    n_rk[nd] = krk[r];
-                    n_s[nd] = ksc[r];
+                    n_rk[nd] = me.rk;
+                    n_s[nd] = sv_s[e];
                     uint32_t cm = 0xFFFFFFFFu;
                     if (kind != DT_NGRAM_NONE && t < d) {
                         const int pj = t == 1 ? 0 : n_tidx[fbase + p];
@@ -491,12 +610,15 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
                     n_cmask[nd] = cm;
                 }
             }
+            __builtin_amdgcn_wave_barrier();
+            fbase = nb;
+            nb += keep;
+            f = keep;
         }
-        __syncthreads();
-        fbase = nb;
-        nb += keep;
-        f = keep;
+        if (lane == 0) misc[0] = nb;
     }
+    __syncthreads();
+    nb = *(volatile int*)&misc[0];
 
     // ---- 4. verification budget
     int n_sel = nb;
