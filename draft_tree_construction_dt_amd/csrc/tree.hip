@@ -507,15 +507,21 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
         int fbase = 0;    // BFS index of the first frontier node
         const uint32_t root_mask = kind == DT_NGRAM_NONE ? 0xFFFFFFFFu : s_vmask[0];
         const float inv_k = 1.0f / (float)k;
+        // per-depth constants, lane t-1 holding depth t's: normaliser and the
+        // mask of children with a finite logit
+        const double lse_l = lane < d ? s_lse[lane] : 0.0;
+        uint32_t live_l = 0;
+        if (lane < d)
+            for (int j = 0; j < k; ++j) live_l |= (uint32_t)(s_tx[lane * k + j] != -INFINITY) << j;
         for (int t = 1; t <= d; ++t) {
             const int tk = (t - 1) * k;
             const int m = f * k;
             const int R = (m + 63) >> 6;
-            const double lse_t = s_lse[t - 1];
-            const uint32_t live =
-                (uint32_t)__ballot(lane < k && s_tx[tk + (lane < k ? lane : 0)] != -INFINITY);
+            const double lse_t = readlane_d(lse_l, t - 1);
+            const uint32_t live = (uint32_t)__builtin_amdgcn_readlane((int)live_l, t - 1);
             double krk[RM], ksc[RM];
             uint32_t ktie[RM];
+            int kgp[RM];
             bool kok[RM];
             int nvalid = 0, nfirst = 0;
             double firstmin = INFINITY;
@@ -526,6 +532,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
                 krk[r] = -INFINITY;
                 ksc[r] = -INFINITY;
                 ktie[r] = 0xFFFFFFFFu;
+                kgp[r] = 0;
                 if (r < R && slot < m) {
                     const int p = (int)(((float)slot + 0.5f) * inv_k);   // exact: slot < 2^11
                     const int j = slot - p * k;
@@ -540,6 +547,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
                         ps = n_s[nd];
                         gp = n_tidx[nd];
                     }
+                    kgp[r] = gp;
                     const uint32_t rowv = cm & live;
                     ok = (rowv >> j) & 1u;
                     first = ok && j == __builtin_ctz(rowv);
@@ -566,7 +574,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
                 const unsigned long long bal = __ballot(in);
                 if (in) {
                     const int e = ns + lanes_below(bal);
-                    sv_key[e] = SurvKey{krk[r], ktie[r], (uint32_t)(r * 64 + lane)};
+                    sv_key[e] = SurvKey{krk[r], ktie[r], (uint32_t)(r * 64 + lane) | ((uint32_t)kgp[r] << 16)};
                     sv_s[e] = ksc[r];
                 }
                 ns += __popcll(bal);
@@ -592,21 +600,20 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
                     rank += (o.rk > me.rk) | ((o.rk == me.rk) & (o.tie < me.tie));
                 }
                 if (e < ns && rank < keep) {
-                    const int slot = (int)me.slot;
-                    const int p = (int)(((float)slot + 0.5f) * inv_k);
+                    const int slot = (int)(me.slot & 0xFFFFu);
+                    const int pj = (int)(me.slot >> 16);          // parent's index in T_{t-2}
+                    const int p = (int)(me.tie & 63u);
                     const int j = slot - p * k;
                     const int nd = nb + rank;
-                    n_tok[nd] = s_ttok[tk + j];
+                    uint32_t cm = 0xFFFFFFFFu;
+                    if (kind != DT_NGRAM_NONE && t < d) cm = s_vmask[ctx_index(kind, k, t + 1, t == 1 ? 0 : pj, j)];
+                    const double sc = sv_s[e];
+                    n_tok[nd] = (int)(me.tie >> 6);
                     n_par[nd] = t == 1 ? -1 : fbase + p;
                     n_dep[nd] = t;
                     n_tidx[nd] = j;
                     n_rk[nd] = me.rk;
-                    n_s[nd] = sv_s[e];
-                    uint32_t cm = 0xFFFFFFFFu;
-                    if (kind != DT_NGRAM_NONE && t < d) {
-                        const int pj = t == 1 ? 0 : n_tidx[fbase + p];
-                        cm = s_vmask[ctx_index(kind, k, t + 1, pj, j)];
-                    }
+                    n_s[nd] = sc;
                     n_cmask[nd] = cm;
                 }
             }
