@@ -16,7 +16,8 @@
 // wave: an exact top-k by threshold filtering -- an element enters the
 // wave's LDS buffer only if its key beats the current k-th key -- with the
 // threshold seeded from the k-th largest of the 64 lane maxima of the first
-// batch and raised by selections of the buffer.
+// batch (a ballot radix selection, no data exchange between lanes) and raised
+// by selections of the buffer.
 #include "common.h"
 
 namespace dt {
@@ -43,19 +44,21 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// k-th largest of one float per lane (bitonic sort across the wave, descending).
-__device__ __forceinline__ float wave_kth_largest(float v, int k, int lane) {
+// A threshold below which no element can be among the wave's k largest:
+// the largest value t with ord(t) a multiple of 2^16 such that at least k
+// lanes hold a value >= t, found bit by bit with ballots (the 16 high bits of
+// ord; exact for bf16 data, whose low 16 bits are zero).  Lanes' padding
+// values are -inf, so the result is never below -inf.
+__device__ __forceinline__ float wave_threshold(float v, int k) {
+    const uint32_t u = ord_bits(__float_as_uint(v + 0.0f));
+    uint32_t t = 0;
 #pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const float o = __shfl_xor(v, stride);
-            const bool desc = (lane & size) == 0;
-            const bool lower = (lane & stride) == 0;
-            v = (desc == lower) ? fmaxf(v, o) : fminf(v, o);
-        }
+    for (int b = 31; b >= 16; --b) {
+        const uint32_t c = t | (1u << b);
+        if (__popcll(__ballot(u >= c)) >= k) t = c;
     }
-    return __shfl(v, k - 1);
+    const uint32_t floor_ord = ord_bits(0xFF800000u);              // -inf
+    return t <= floor_ord ? -INFINITY : __uint_as_float(unord_bits(t));
 }
 
 struct WaveState {
@@ -72,13 +75,22 @@ struct WaveState {
 // with a larger key (keys are unique: ids differ).
 __device__ __forceinline__ void wave_select(unsigned long long* buf, WaveState& st, int k, int lane) {
     const int n = st.cnt;
+    const int n8 = (n + 7) & ~7;
+    // pad to a multiple of eight with empty keys (0 beats nothing); a wave's
+    // LDS accesses complete in order, so the reads below see these writes
+    if (lane < n8 - n) buf[n + lane] = 0ull;
     const unsigned long long a = lane < n ? buf[lane] : 0ull;
     const unsigned long long b = lane + 64 < n ? buf[lane + 64] : 0ull;
     int ra = 0, rb = 0;
-    for (int j = 0; j < n; ++j) {
-        const unsigned long long v = buf[j];
-        ra += v > a;
-        rb += v > b;
+    for (int j = 0; j < n8; j += 8) {            // eight independent broadcast reads per step
+        unsigned long long v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = buf[j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            ra += v[u] > a;
+            rb += v[u] > b;
+        }
     }
     __builtin_amdgcn_wave_barrier();
     if (lane < n && ra < k) buf[ra] = a;
@@ -92,13 +104,54 @@ __device__ __forceinline__ void wave_select(unsigned long long* buf, WaveState& 
     }
 }
 
-// Fold NE elements per lane into the lane's softmax state and the wave's
-// top-k buffer.  id0[u] is the row index of element u*EPV, vok[u] whether
-// vector u exists (padding elements are -inf and never enter the top-k).
+// Rare path of consume: some lane's batch holds an element that reaches the
+// threshold.  The lane's elements are staged in LDS (element-major, so the
+// 64 lanes hit 64 different banks) and visited by a compact runtime loop, one
+// round per candidate of the lane that holds the most; the common path thus
+// stays a short straight loop.  Element e of the batch is vector e / EPV,
+// lane element e % EPV; its row index is id0 + (e / EPV) * id_step + e % EPV.
 template <int NE, int EPV>
-__device__ __forceinline__ void consume(const float (&xs)[NE], const int (&id0)[NE / EPV],
+__device__ __forceinline__ void insert_candidates(const float (&xs)[NE], int id0, int id_step,
+                                                  const bool (&vok)[NE / EPV], WaveState& st,
+                                                  unsigned long long* buf, float* stage, int k,
+                                                  int trig, int lane) {
+    static_assert(NE <= 32, "one pass mask bit per element");
+    uint32_t pm = 0;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) pm |= (uint32_t)(vok[e / EPV] && xs[e] >= st.thv) << e;
+    if (pm) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) stage[e * 64 + lane] = xs[e];
+    }
+    while (__ballot(pm != 0u) != 0ull) {
+        const bool has = pm != 0u;
+        const int e = has ? __builtin_ctz(pm) : 0;
+        pm &= pm - 1u;
+        const float x = has ? stage[e * 64 + lane] : -INFINITY;
+        const uint32_t id = (uint32_t)(id0 + (e / EPV) * id_step + (e % EPV));
+        bool q = has && (x > st.thv || (x == st.thv && id < st.thid));
+        unsigned long long bal = __ballot(q);
+        if (bal == 0ull) continue;
+        if (st.cnt + 64 > CAP) {
+            wave_select(buf, st, k, lane);
+            q = q && (x > st.thv || (x == st.thv && id < st.thid));
+            bal = __ballot(q);
+        }
+        if (q) buf[st.cnt + lanes_below(bal)] = make_key(x, id);
+        st.cnt += __popcll(bal);
+    }
+    if (st.cnt >= trig) wave_select(buf, st, k, lane);
+}
+
+// Fold NE elements per lane into the lane's softmax state and the wave's
+// top-k buffer.  Element e is vector e / EPV (vok: whether it exists; padding
+// elements are -inf), lane element e % EPV, row index
+// id0 + (e / EPV) * id_step + e % EPV.
+template <int NE, int EPV>
+__device__ __forceinline__ void consume(const float (&xs)[NE], int id0, int id_step,
                                         const bool (&vok)[NE / EPV], WaveState& st,
-                                        unsigned long long* buf, int k, int trig, int lane) {
+                                        unsigned long long* buf, float* stage, float* seeds,
+                                        int k, int trig, int lane, int wave) {
     float bm = xs[0];
 #pragma unroll
     for (int e = 1; e < NE; ++e) bm = fmaxf(bm, xs[e]);
@@ -116,29 +169,24 @@ __device__ __forceinline__ void consume(const float (&xs)[NE], const int (&id0)[
     }
 
     if (st.fresh) {
-        st.thv = wave_kth_largest(bm, k, lane);   // k lanes hold an element >= this value
+        // Every wave seeds a threshold from its first batch: k of its lanes
+        // hold an element >= the seed.  Any k elements of the row bound the
+        // row's k-th largest from below, so no element under the largest of
+        // the four seeds can be among the row's top k, and every wave filters
+        // with that one.  (All waves of the workgroup take their first batch
+        // in the same call, so the barrier is reached by all of them.)
+        const float t = wave_threshold(bm, k);
+        if (lane == 0) seeds[wave] = t;
+        __syncthreads();
+        float tm = seeds[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) tm = fmaxf(tm, seeds[w]);
+        st.thv = tm;
         st.thid = 0xFFFFFFFFu;
         st.fresh = false;
     }
     if (__ballot(bm >= st.thv) == 0ull) return;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-        const float x = xs[e];
-        if (__ballot(x >= st.thv) == 0ull) continue;
-        const int u = e / EPV;
-        const uint32_t id = (uint32_t)(id0[u] + (e % EPV));
-        bool q = vok[u] && (x > st.thv || (x == st.thv && id < st.thid));
-        unsigned long long bal = __ballot(q);
-        if (bal == 0ull) continue;
-        if (st.cnt + 64 > CAP) {
-            wave_select(buf, st, k, lane);
-            q = q && (x > st.thv || (x == st.thv && id < st.thid));
-            bal = __ballot(q);
-        }
-        if (q) buf[st.cnt + lanes_below(bal)] = make_key(x, id);
-        st.cnt += __popcll(bal);
-    }
-    if (st.cnt >= trig) wave_select(buf, st, k, lane);
+    insert_candidates<NE, EPV>(xs, id0, id_step, vok, st, buf, stage, k, trig, lane);
 }
 
 template <bool BF16>
@@ -174,6 +222,8 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
     constexpr int NE = U * EPV;
 
     __shared__ unsigned long long s_buf[kWaves][CAP];
+    __shared__ float s_stage[kWaves][NE * 64];   // rare-path staging of a batch
+    __shared__ float s_seeds[kWaves];             // first-batch thresholds of the waves
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -199,6 +249,7 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
     }
     const vec4* vbase = reinterpret_cast<const vec4*>(a.logits);
     unsigned long long* buf = s_buf[wave];
+    float* stage = s_stage[wave];
 
     WaveState st;
     st.m = -INFINITY;
@@ -221,16 +272,14 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
             vec4 nxt[U];
             if (bi + 1 < nbat) load_batch<BF16>(nxt, vbase, q0 + per_batch, v_hi);
             float xs[NE];
-            int id0[U];
             bool vok[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t q = q0 + (int64_t)u * kThreads;
                 unpack<BF16>(cur[u], xs + u * EPV);
-                id0[u] = (int)(q * EPV - row0);
-                vok[u] = q < v_hi;
+                vok[u] = q0 + (int64_t)u * kThreads < v_hi;
             }
-            consume<NE, EPV>(xs, id0, vok, st, buf, k, trig, lane);
+            consume<NE, EPV>(xs, (int)(q0 * EPV - row0), kThreads * EPV, vok, st, buf, stage, s_seeds, k, trig, lane,
+                             wave);
             if (bi + 1 < nbat) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) cur[u] = nxt[u];
@@ -242,7 +291,6 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
         const int64_t n1 = s1_hi - s1_lo, n2 = s2_hi - s2_lo;       // each < EPV
         if (n1 + n2 > 0) {
             float xs[1];
-            int id0[1];
             bool vok[1];
             const int64_t g = tid < n1 ? s1_lo + tid : s2_lo + (tid - n1);
             vok[0] = tid < n1 + n2;
@@ -255,8 +303,7 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
                 }
             }
             xs[0] = x;
-            id0[0] = vok[0] ? (int)(g - row0) : 0;
-            consume<1, 1>(xs, id0, vok, st, buf, k, trig, lane);
+            consume<1, 1>(xs, vok[0] ? (int)(g - row0) : 0, 0, vok, st, buf, stage, s_seeds, k, trig, lane, wave);
         }
     }
 
