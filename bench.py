@@ -8,15 +8,19 @@ independent requests, V=151936, d=8 draft positions, top-k 10, width 8,
 budget 64, bf16 logits (N(0,3) plus a log Zipf(1.1) prior, coherence-planted),
 a shared open-addressing trigram table of 2^22 slots with 16 successors.
 Inputs rotate over several distinct sets totalling more than three times
-the 256 MB Infinity Cache, all resident in HBM before timing starts.  The
-single-request case (B=1, same shape) is timed as well and reported under
-"b1".  Prints one JSON line.
+the 256 MB Infinity Cache, all resident in HBM before timing starts.
+Consecutive calls alternate over --streams HIP streams (default 2), each
+with its own workspace and outputs, so the latency-bound tree kernels of one
+batch overlap the bandwidth-bound sweep of the next, as a serving loop would
+run them; the one-stream figures are reported as well ("single_stream").
+The single-request case (B=1, same shape) is timed the same two ways and
+reported under "b1".  Prints one JSON line.
 
 Roofline: the vocabulary sweep kernel dominates; its duration is measured
 live with HIP events that the library records around that kernel on the
-launch stream (every n-th launch of the timed loop, so that the event
-records barely perturb the throughput figure), and its algorithmic bytes
-are the logits it must read (B*d*V*2 per launch).
+launch stream (every n-th launch of the one-stream timed loop, where no other
+kernel shares the GPU with it, so that the events time the kernel itself),
+and its algorithmic bytes are the logits it must read (B*d*V*2 per launch).
 """
 
 import argparse
@@ -49,6 +53,8 @@ def parse():
     ap.add_argument("--b1-steps", type=int, default=2000, help="timed single-request calls")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests the oracle builds for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="HIP streams the calls alternate over (consecutive batches in flight together)")
     ap.add_argument("--event-every", type=int, default=8,
                     help="bracket every n-th B=64 sweep launch with timing events")
     ap.add_argument("--seed", type=int, default=0)
@@ -157,74 +163,84 @@ def main():
     logits = bd.logits_tensor(prob, dev)                      # [sets*64][d][V] bf16
     ctx = torch.from_numpy(prob.ctx).to(dev)
     ngram = bd.upload_ngram(prob.ngram, dev)
-    stream = torch.cuda.current_stream()
     lib = bd._load()
     fn = lib.dt_build_tree
+    nstream = max(1, args.streams)
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream(device=dev) for _ in range(nstream - 1)]
 
-    def params(B, first):
+    def params(B, first, stream):
         p = bd.Params(B=B, V=prob.V, d=prob.d, k=prob.k, W=prob.W, budget=prob.budget,
                       dtype=bd.DT_DTYPE_BF16, mode=bd.DT_MODE_DART, ctx=ctx[first:first + B], stream=stream,
                       sweep_chunks=args.sweep_chunks if B > 1 else 0)
         p.workspace = torch.empty(max(bd.dt_workspace_size(p), 16), dtype=torch.uint8, device=dev)
         return p
 
-    # ---- B = 64: rotate over the sets
-    sets = [params(BATCH, s * BATCH) for s in range(args.sets)]
-    out = bd.alloc_tree_out(BATCH, prob.budget, dev)
-    ng_c, out_c = ngram._c(), out._c()
-    set_c = [s._c() for s in sets]
-    set_ptr = [logits[s * BATCH].data_ptr() for s in range(args.sets)]
-    logit_bytes = BATCH * prob.d * prob.V * 2
-    for i in range(args.warmup):
-        st = fn(set_ptr[i % args.sets], ctypes.byref(ng_c), ctypes.byref(set_c[i % args.sets]),
-                ctypes.byref(out_c))
-        if st != 0:
-            raise bd.DtError(st, "dt_build_tree")
-    torch.cuda.synchronize()
-
-    K = args.steps
+    ng_c = ngram._c()
     tev = TimingEvents()
+
+    def run(B, inputs, K, warmup, S, events_every=0):
+        """K calls of dt_build_tree; call i takes input i % len(inputs) on stream
+        i % S, with a workspace and output buffers of its own per (input, stream)
+        so that calls in flight on different streams share nothing.  Returns
+        the wall time of the K calls and, if events_every, the sweep durations
+        of every events_every-th call."""
+        keep = []
+        pcs = []
+        for si in range(S):
+            row = []
+            for first in inputs:
+                q = params(B, first, streams[si])
+                keep.append(q)
+                row.append(q._c())
+            pcs.append(row)
+        outs = [bd.alloc_tree_out(B, prob.budget, dev) for _ in range(S)]
+        outs_c = [o._c() for o in outs]
+        ptrs = [logits[first].data_ptr() for first in inputs]
+        n = len(inputs)
+
+        def call(i):
+            st = fn(ptrs[i % n], ctypes.byref(ng_c), ctypes.byref(pcs[i % S][i % n]), ctypes.byref(outs_c[i % S]))
+            if st != 0:
+                raise bd.DtError(st, "dt_build_tree")
+
+        for i in range(warmup):
+            call(i)
+        torch.cuda.synchronize()
+        raw = {}
+        if events_every:
+            raw = {i: (tev.create(), tev.create()) for i in range(0, K, events_every)}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            pc = pcs[i % S][i % n]
+            pc.prof_event_start, pc.prof_event_stop = raw.get(i, (None, None))
+            call(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [tev.elapsed_ms(x, y) for x, y in raw.values()]
+        for x, y in raw.values():
+            tev.destroy(x)
+            tev.destroy(y)
+        return wall, ms
+
+    # ---- B = 64: rotate over the sets; the timed run brackets every
+    #      event_every-th sweep launch with events (the roofline figure)
+    logit_bytes = BATCH * prob.d * prob.V * 2
+    set_first = [s * BATCH for s in range(args.sets)]
+    K = args.steps
     every = max(1, args.event_every)
-    timed = list(range(0, K, every))
-    raw = {i: (tev.create(), tev.create()) for i in timed}
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(K):
-        pc = set_c[i % args.sets]
-        pc.prof_event_start, pc.prof_event_stop = raw.get(i, (None, None))
-        fn(set_ptr[i % args.sets], ctypes.byref(ng_c), ctypes.byref(pc), ctypes.byref(out_c))
-    torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
-    for pc in set_c:
-        pc.prof_event_start = pc.prof_event_stop = None
-    sweep_ms = [tev.elapsed_ms(a, b) for a, b in raw.values()]
-    for a, b in raw.values():
-        tev.destroy(a)
-        tev.destroy(b)
-    sweep_avg_s = sum(sweep_ms) / len(sweep_ms) / 1e3
+    t_total, _ = run(BATCH, set_first, K, args.warmup, nstream)
     ms_per_step = t_total / K * 1e3
     trees_per_s = BATCH * K / t_total
+    # one stream: the kernels run alone, so the sweep events time the kernel itself
+    t_one, sweep_ms = run(BATCH, set_first, K, args.warmup, 1, events_every=every)
+    sweep_avg_s = sum(sweep_ms) / len(sweep_ms) / 1e3
 
     # ---- B = 1: one request per call, rotating over every request of every set
     nreq = BATCH * args.sets
-    one = [params(1, r) for r in range(nreq)]
-    out1 = bd.alloc_tree_out(1, prob.budget, dev)
-    out1_c = out1._c()
-    one_c = [q._c() for q in one]
-    one_ptr = [logits[r].data_ptr() for r in range(nreq)]
-    for i in range(min(200, args.b1_steps)):
-        fn(one_ptr[i % nreq], ctypes.byref(ng_c), ctypes.byref(one_c[i % nreq]), ctypes.byref(out1_c))
-    torch.cuda.synchronize()
     K1 = args.b1_steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t1 = time.perf_counter()
-    e0.record(stream)
-    for i in range(K1):
-        fn(one_ptr[i % nreq], ctypes.byref(ng_c), ctypes.byref(one_c[i % nreq]), ctypes.byref(out1_c))
-    e1.record(stream)
-    torch.cuda.synchronize()
-    b1_wall = time.perf_counter() - t1
-    b1_gpu_ms = e0.elapsed_time(e1)
+    b1_wall, _ = run(1, list(range(nreq)), K1, min(200, K1), nstream)
+    b1_one, _ = run(1, list(range(nreq)), K1, min(200, K1), 1)
 
     achieved = logit_bytes / sweep_avg_s / 1e9
     traffic = stored_traffic()
@@ -250,11 +266,19 @@ def main():
             "input_bytes_rotated": logit_bytes * args.sets,
         },
         "us_per_tree": t_total / (BATCH * K) * 1e6,
+        "streams": nstream,
+        "single_stream": {
+            "trees_per_s": BATCH * K / t_one,
+            "ms_per_step": t_one / K * 1e3,
+            "us_per_tree": t_one / (BATCH * K) * 1e6,
+        },
         "b1": {
             "workload": "same shape, B=1 (one request per call)",
             "trees_per_s": K1 / b1_wall,
-            "us_per_tree_wall": b1_wall / K1 * 1e6,
-            "us_per_tree_gpu": b1_gpu_ms / K1 * 1e3,
+            "us_per_tree": b1_wall / K1 * 1e6,
+            "streams": nstream,
+            "single_stream_trees_per_s": K1 / b1_one,
+            "single_stream_us_per_call": b1_one / K1 * 1e6,
             "steps": K1,
         },
         "roofline": {
@@ -267,7 +291,8 @@ def main():
             "traffic": traffic,
             "avg_launch_us": sweep_avg_s * 1e6,
             "timing": f"HIP events recorded by the library around every {every}-th sweep launch of the "
-                      f"timed loop ({len(timed)} launches) on its stream, created with hipEventDisableSystemFence",
+                      f"one-stream timed loop ({len(sweep_ms)} launches) on its stream, created with "
+                      f"hipEventDisableSystemFence",
             "algorithmic_bytes_per_launch": logit_bytes,
         },
     }

@@ -34,23 +34,39 @@ SweepPlan plan_sweep(const dt_params* p) {
     return s;
 }
 
+int n_contexts(int kind, int d, int k) {
+    if (kind == DT_NGRAM_NONE) return 0;
+    if (kind == DT_NGRAM_HASH_TRIGRAM) return d == 1 ? 1 : 1 + k + (d - 2) * k * k;
+    return 1 + (d - 1) * k;
+}
+
 WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s) {
     WorkspacePlan w{};
     const int64_t n = s.rows * s.C * kWaves;     // one partial list per sweep wave
-    w.off_m = 0;
-    w.off_s = (size_t)round_up(n * 4, 256);
-    w.off_keys = (size_t)round_up((int64_t)w.off_s + n * 8, 256);
-    w.total = (size_t)round_up((int64_t)w.off_keys + n * p->k * 8, 256);
-    if (n == 0) w.total = 0;
+    const int64_t rows = s.rows, k = p->k;
+    w.n_ctx_cap = n_contexts(DT_NGRAM_HASH_TRIGRAM, p->d, p->k);   // the largest kind
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t o = round_up(off, 256);
+        off = o + bytes;
+        return (size_t)o;
+    };
+    w.off_m = take(n * 4);
+    w.off_s = take(n * 8);
+    w.off_keys = take(n * k * 8);
+    w.off_lse = take(rows * 8);
+    w.off_ttok = take(rows * k * 4);
+    w.off_tx = take(rows * k * 4);
+    w.off_vmask = take((int64_t)p->B * w.n_ctx_cap * 4);
+    w.off_g = take(p->mode == DT_MODE_DARTREE ? rows * k * k * 8 : 0);
+    w.total = (size_t)round_up(off, 256);
     return w;
 }
 
 TreePlan plan_tree(const dt_params* p, int kind) {
     TreePlan P{};
     const int d = p->d, k = p->k, W = p->W;
-    if (kind == DT_NGRAM_NONE) P.n_ctx = 0;
-    else if (kind == DT_NGRAM_HASH_TRIGRAM) P.n_ctx = d == 1 ? 1 : 1 + k + (d - 2) * k * k;
-    else P.n_ctx = 1 + (d - 1) * k;
+    P.n_ctx = n_contexts(kind, d, k);
     P.max_nodes = d * W;
     P.max_cand = W * k;
     int off = 0;
@@ -64,16 +80,11 @@ TreePlan plan_tree(const dt_params* p, int kind) {
     P.off_g = take(p->mode == DT_MODE_DARTREE ? d * k * k * 8 : 0, 8);
     P.off_ttok = take(d * k * 4, 4);
     P.off_tx = take(d * k * 4, 4);
-    P.off_ctxbase = 0;
     P.off_vmask = take(P.n_ctx * 4, 4);
     P.off_misc = take(kMiscInts * 4, 4);
-    P.off_sv_key = take(P.max_cand * 16, 16);
-    P.off_sv_s = take(P.max_cand * 8, 8);
-    // node arrays; the per-wave merge scratch of step 1 reuses this space
-    const int region = (int)round_up(off, 16);
-    off = region;
+    P.off_sv_key = take((P.max_cand + 16) * 16, 16);  // + a block of sentinels
+    P.off_sv_s = take((P.max_cand + 16) * 16, 16);
     const int nn = P.max_nodes;
-    P.off_nodes = region;
     P.off_n_rk = take(nn * 8, 8);
     P.off_n_s = take(nn * 8, 8);
     P.off_n_tok = take(nn * 4, 4);
@@ -83,9 +94,7 @@ TreePlan plan_tree(const dt_params* p, int kind) {
     P.off_n_cctx = take(nn * 4, 4);
     P.off_n_new = take(nn * 4, 4);
     P.off_n_out = take(nn * 4, 4);
-    P.off_merge = region;
-    const int merge_end = region + kMergeWaves * kMergeKeysPerRow * 8;
-    P.total = (int)round_up(off > merge_end ? off : merge_end, 16);
+    P.total = (int)round_up(off, 16);
     return P;
 }
 
@@ -204,34 +213,57 @@ extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngr
     if ((st = launch_sweep_for(logits, p, s, w)) != DT_OK) return st;
 
     char* ws = (char*)p->workspace;
+    PrepArgs pa{};
+    pa.B = p->B;
+    pa.d = p->d;
+    pa.k = p->k;
+    pa.L = s.C * kWaves;                          // partial lists per row
+    pa.mode = p->mode;
+    pa.R = p->R;
+    pa.n_ctx = w.n_ctx_cap;
+    pa.ctx = p->ctx;
+    pa.part_m = (const float*)(ws + w.off_m);
+    pa.part_s = (const double*)(ws + w.off_s);
+    pa.part_keys = (const unsigned long long*)(ws + w.off_keys);
+    pa.ng.kind = ngram->kind;
+    pa.ng.V = p->V;
+    pa.ng.min_logp = ngram->min_logp;
+    pa.ng.dense = ngram->dense_logp;
+    pa.ng.row_ptr = ngram->row_ptr;
+    pa.ng.col = ngram->col;
+    pa.ng.csr_logp = ngram->csr_logp;
+    pa.ng.keys = (const unsigned long long*)ngram->keys;
+    pa.ng.succ = ngram->succ;
+    pa.ng.hash_logp = ngram->hash_logp;
+    pa.ng.cap = ngram->cap;
+    pa.ng.S = ngram->S;
+    pa.E = p->E;
+    pa.F = p->F;
+    pa.lse = (double*)(ws + w.off_lse);
+    pa.ttok = (int32_t*)(ws + w.off_ttok);
+    pa.tx = (float*)(ws + w.off_tx);
+    pa.vmask = (uint32_t*)(ws + w.off_vmask);
+    pa.g = (double*)(ws + w.off_g);
+    // the k^2 trigram contexts of a depth are split over workgroups of
+    // kPrepContexts lookups
+    pa.nsplit = ngram->kind == DT_NGRAM_HASH_TRIGRAM ? (int)ceil_div((int64_t)p->k * p->k, kPrepContexts) : 1;
+    if (launch_prep(pa, (hipStream_t)p->stream) != hipSuccess) return DT_ERR_HIP;
+
     TreeArgs ta{};
     ta.B = p->B;
-    ta.V = p->V;
     ta.d = p->d;
     ta.k = p->k;
     ta.W = p->W;
     ta.budget = p->budget;
     ta.mode = p->mode;
-    ta.C = s.C * kWaves;                          // partial lists per row
-    ta.R = p->R;
     ta.mask_words = (p->budget + 31) / 32;
-    ta.ctx = p->ctx;
-    ta.part_m = (const float*)(ws + w.off_m);
-    ta.part_s = (const double*)(ws + w.off_s);
-    ta.part_keys = (const unsigned long long*)(ws + w.off_keys);
     ta.ng_kind = ngram->kind;
-    ta.min_logp = ngram->min_logp;
-    ta.dense = ngram->dense_logp;
-    ta.row_ptr = ngram->row_ptr;
-    ta.col = ngram->col;
-    ta.csr_logp = ngram->csr_logp;
-    ta.keys = (const unsigned long long*)ngram->keys;
-    ta.succ = ngram->succ;
-    ta.hash_logp = ngram->hash_logp;
-    ta.cap = ngram->cap;
-    ta.S = ngram->S;
-    ta.E = p->E;
-    ta.F = p->F;
+    ta.n_ctx = w.n_ctx_cap;                       // per-request stride of vmask
+    ta.lse = pa.lse;
+    ta.ttok = pa.ttok;
+    ta.tx = pa.tx;
+    ta.vmask = pa.vmask;
+    ta.g = pa.g;
     ta.n_nodes = out->n_nodes;
     ta.tokens = out->tokens;
     ta.parents = out->parents;

@@ -17,12 +17,13 @@ constexpr int kMaxCandidates = 1024;   // W * k
 constexpr int kMaxV = 1 << 26;         // token ids fit the 26-bit field of the tie key
 constexpr int kThreads = 256;          // sweep and merge kernels: four wave64s
 constexpr int kWaves = kThreads / 64;
-constexpr int kTreeThreads = 1024;     // tree kernel: sixteen wave64s per request
+constexpr int kTreeThreads = 256;      // tree kernel: four wave64s per request
 constexpr int kTreeWaves = kTreeThreads / 64;
-constexpr int kMergeWaves = 8;         // tree-kernel waves that merge the sweep partials
+constexpr int kPrepRows = 3;           // rows a prep workgroup merges: children, parents, grandparents
+constexpr int kPrepContexts = 256;     // continuity contexts per prep workgroup (one per thread)
 constexpr int kMiscInts = 32;          // tree-kernel counters (0..3) and scan scratch (16..31)
 constexpr int kTreeLdsLimit = 64 * 1024;
-constexpr int kMergeKeysPerRow = 256;  // C * 4 * k bound: per-wave merge scratch in the tree kernel
+constexpr int kMergeKeysPerRow = 256;  // C * 4 * k bound: per-wave merge scratch
 constexpr int kSweepVecsPerThread = 4; // 16-byte vectors each thread holds per batch
 constexpr int kSweepCap = 128;         // per-wave candidate buffer of the sweep
 
@@ -52,31 +53,35 @@ struct SweepPlan {
     int64_t rows;
 };
 
-// Workspace: per (row, chunk, sweep wave) partial results of the sweep.
+// Workspace: per (row, chunk, sweep wave) partial results of the sweep, then
+// what the prep kernel derives from them for the tree kernel.
 //   part_m    float  [rows][C*4]      running max of the wave's elements
 //   part_s    double [rows][C*4]      sum exp(x - part_m) over them
 //   part_keys uint64 [rows][C*4][k]   their top-k keys, descending; 0 pads
+//   lse       double [rows]           log-softmax normaliser of each row
+//   ttok      int32  [rows][k]        top-k token ids (T_i), value desc, id asc
+//   tx        float  [rows][k]        their logits
+//   vmask     uint32 [B][n_ctx_cap]   admissible children of every context
+//   g         double [rows][k][k]     parent-conditioned terms (DARTree only)
 struct WorkspacePlan {
-    size_t off_m, off_s, off_keys, total;
+    size_t off_m, off_s, off_keys, off_lse, off_ttok, off_tx, off_vmask, off_g, total;
+    int n_ctx_cap;      // contexts per request the vmask area holds (the trigram count)
 };
 
 // Shared-memory plan of the tree kernel (byte offsets into dynamic LDS).
 struct TreePlan {
-    int n_ctx;          // continuity contexts looked up before the depth loop
+    int n_ctx;          // continuity contexts of the table kind
     int max_nodes;      // d * W
     int max_cand;       // W * k
     int off_lse;        // double [d]
     int off_ttok;       // int    [d][k]   top-k ids per position
     int off_tx;         // float  [d][k]   their logits
-    int off_ctxbase;    // int    [d + 2]  first context of each depth
     int off_vmask;      // uint32 [n_ctx]  admissible children (bit j = T[t-1][j])
     int off_g;          // double [d][k][k] parent-conditioned terms (DARTree)
-    int off_nodes;      // node arrays (aliased by the merge scratch)
     int off_n_tok, off_n_par, off_n_dep, off_n_tidx, off_n_cctx, off_n_new, off_n_out;
     int off_n_rk, off_n_s;
-    int off_merge;      // uint64 [kMergeWaves][kMergeKeysPerRow] (aliases the node arrays)
-    int off_sv_key;     // 16-byte survivor keys [W*k] of the depth loop
-    int off_sv_s;       // double [W*k] their cumulative scores
+    int off_sv_key;     // 16-byte survivor keys [W*k + 16] of the depth loop
+    int off_sv_s;       // 16-byte survivor records [W*k + 16]: score and children's mask
     int off_misc;       // int counters
     int total;
 };
@@ -92,13 +97,10 @@ struct SweepArgs {
     unsigned long long* part_keys;
 };
 
-struct TreeArgs {
-    int B, V, d, k, W, budget, mode, C, R, mask_words;
-    const int32_t* ctx;
-    const float* part_m;
-    const double* part_s;
-    const unsigned long long* part_keys;
-    int ng_kind;
+// the N-gram table as the kernels see it
+struct NGramArgs {
+    int kind;
+    int V;
     float min_logp;
     const float* dense;
     const int32_t* row_ptr;
@@ -109,8 +111,31 @@ struct TreeArgs {
     const float* hash_logp;
     long long cap;
     int S;
+};
+
+struct PrepArgs {
+    int B, d, k, L, mode, R, n_ctx, nsplit;
+    const int32_t* ctx;
+    const float* part_m;
+    const double* part_s;
+    const unsigned long long* part_keys;
+    NGramArgs ng;
     const float* E;
     const float* F;
+    double* lse;
+    int32_t* ttok;
+    float* tx;
+    uint32_t* vmask;
+    double* g;
+};
+
+struct TreeArgs {
+    int B, d, k, W, budget, mode, mask_words, ng_kind, n_ctx;
+    const double* lse;
+    const int32_t* ttok;
+    const float* tx;
+    const uint32_t* vmask;
+    const double* g;
     int32_t* n_nodes;
     int32_t* tokens;
     int32_t* parents;
@@ -134,9 +159,11 @@ struct MergeArgs {
 SweepPlan plan_sweep(const dt_params* p);
 WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s);
 TreePlan plan_tree(const dt_params* p, int ngram_kind);
+int n_contexts(int ngram_kind, int d, int k);
 
 // launchers (sweep.hip, tree.hip)
 hipError_t launch_sweep(const SweepArgs& a, int64_t rows, int dtype, hipStream_t stream);
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 

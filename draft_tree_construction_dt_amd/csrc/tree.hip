@@ -1,35 +1,41 @@
-// Tree construction: one 1024-thread workgroup per request, all state in LDS.
+// Tree construction: two kernels after the vocabulary sweep.
 //
-//  1. Merge the sweep's per-chunk partials of the request's d rows into the
-//     log-softmax normaliser (fp64 merge and log) and the exact top-k list
-//     T_i of every position (DART, arXiv 2601.19278, Fig. 3: a position's
-//     own logit proposes the tokens of its depth).
-//  2. Look up N-gram continuity for every context a frontier node can have
-//     before the depth loop starts.  A depth-t parent carries a token of
-//     T_{t-2} (and, for the trigram, its parent a token of T_{t-3}), so at
-//     most 1 + k + (d-2) k^2 trigram contexts (1 + (d-1) k bigram contexts)
-//     exist; all lookups are issued in parallel and the result is one
-//     admissibility bit per (context, child of T_{t-1}).  In DARTree mode the
-//     parent-conditioned terms E[parent].F[child] for every (T_{t-2}, T_{t-1})
-//     pair come from fp64 MFMA tiles (DARTree "Tree Construction": all
-//     candidates of a depth are scored in one batch).
-//  3. Depth loop: candidates = frontier x T_{t-1}, scored with the lse-free
+// prep_kernel -- one 256-thread workgroup per (request, depth t) [and slice
+// of that depth's contexts], so the latency-bound random reads of the N-gram
+// table and of E/F are spread over many compute units instead of queueing in
+// one:
+//  1. Up to three waves merge the sweep's per-chunk partials of rows t-1 (the
+//     children of depth t), t-2 and t-3 (the tokens a depth-t parent and its
+//     own parent carry) into the log-softmax normaliser (fp64 merge and log)
+//     and the exact top-k list T_i of each row (DART, arXiv 2601.19278,
+//     Fig. 3: a position's own logit proposes the tokens of its depth).  Row
+//     t-1 is written out for the tree kernel.
+//  2. N-gram continuity of every context a depth-t parent can have: a
+//     depth-t parent carries a token of T_{t-2} (and, for the trigram, its
+//     parent a token of T_{t-3}), so depth t has 1, k or k^2 contexts; each
+//     thread looks one up and stores one admissibility bit per child of
+//     T_{t-1}.
+//  3. DARTree: the parent-conditioned terms E[parent].F[child] of depth t
+//     for every (T_{t-2}, T_{t-1}) pair from fp64 MFMA tiles (DARTree "Tree
+//     Construction": all candidates of a depth are scored in one batch).
+//
+// tree_kernel -- one 256-thread workgroup per request, all state in LDS:
+//  4. Depth loop: candidates = frontier x T_{t-1}, scored with the lse-free
 //     key Rk and the cumulative log-score S in fp64; the top-W across the
 //     whole frontier by (Rk desc, token asc, parent rank asc) become the next
 //     frontier (DARTree: "selects the top-W scored nodes across the entire
-//     frontier").  Keys live in registers, ranks come from wave ballots, and
-//     no global memory is touched inside the loop.
-//  4. Budget: best-first selection of the verification tree (DARTree
+//     frontier").  Keys live in registers, ranks come from one wave, and no
+//     global memory is touched inside the loop.
+//  5. Budget: best-first selection of the verification tree (DARTree
 //     abstract).  In DART mode S never increases along a path, so the
 //     best-first set equals the top-`budget` nodes by (S desc, BFS index);
 //     DARTree mode replays best-first literally.
-//  5. Compact in BFS order, remap parents and pack the ancestor mask used by
+//  6. Compact in BFS order, remap parents and pack the ancestor mask used by
 //     tree-attention verification.
 #include "common.h"
 
 namespace dt {
 namespace {
-
 typedef double v4d __attribute__((ext_vector_type(4)));
 extern "C" __device__ double __ockl_wfred_min_f64(double);
 constexpr unsigned long long kEmptyKey = 0xFFFFFFFFFFFFFFFFull;
@@ -83,7 +89,7 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 }
 
 // ---------------------------------------------------------------------------
-// 1. one wave merges the L partial lists of one row
+// one wave merges the L partial lists of one row
 // ---------------------------------------------------------------------------
 __device__ void merge_row(const float* __restrict__ part_m, const double* __restrict__ part_s,
                           const unsigned long long* __restrict__ part_keys, int64_t row, int L, int k,
@@ -156,22 +162,23 @@ __device__ void merge_row(const float* __restrict__ part_m, const double* __rest
         if (keep) scratch[ns + lanes_below(bal)] = kv[r];
         ns += __popcll(bal);
     }
+    // pad to a multiple of eight with empty keys (0 is below every key)
+    const int ns8 = (ns + 7) & ~7;
+    if (lane < ns8 - ns) scratch[ns + lane] = 0ull;
     __builtin_amdgcn_wave_barrier();
     // rank: lane e holds survivor e (blocks of 64) and streams past all of
-    // them (keys are unique)
+    // them, eight independent broadcast reads per step (keys are unique)
     for (int e0 = 0; e0 < ns; e0 += 64) {
         const int e = e0 + lane;
         const unsigned long long v = e < ns ? scratch[e] : ~0ull;
         int rank = 0;
-        int j = 0;
-        for (; j + 8 <= ns; j += 8) {
+        for (int j = 0; j < ns8; j += 8) {
             unsigned long long o[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) o[u] = scratch[j + u];
 #pragma unroll
             for (int u = 0; u < 8; ++u) rank += o[u] > v;
         }
-        for (; j < ns; ++j) rank += scratch[j] > v;
         if (e < ns && rank < k) {
             tok_out[rank] = (int)key_id(v);
             val_out[rank] = key_value(v);
@@ -181,9 +188,9 @@ __device__ void merge_row(const float* __restrict__ part_m, const double* __rest
 }
 
 // ---------------------------------------------------------------------------
-// 2. continuity
+// continuity
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool logp_keeps(const TreeArgs& a, const float* lp, int64_t e) {
+__device__ __forceinline__ bool logp_keeps(const NGramArgs& a, const float* lp, int64_t e) {
     return a.min_logp == -INFINITY || lp == nullptr || lp[e] > a.min_logp;
 }
 
@@ -192,7 +199,7 @@ __device__ __forceinline__ bool logp_keeps(const TreeArgs& a, const float* lp, i
 // 16-byte loads, so a chain costs one memory round trip per 8 slots.
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ long long find_slot(const TreeArgs& a, unsigned long long key) {
+__device__ __forceinline__ long long find_slot(const NGramArgs& a, unsigned long long key) {
     const unsigned long long cm = (unsigned long long)a.cap - 1ull;
     unsigned long long pos = mix64(key) & cm;
     if (a.cap < 8) {
@@ -247,22 +254,21 @@ __device__ __forceinline__ void load_row16(int (&r)[16], const int* p, int n) {
 }
 
 // Bit j set iff child T_{t-1}[j] (finite logit) is admitted after (a2, a1).
-__device__ uint32_t admitted_children(const TreeArgs& a, int a2, int a1, const int* ch, const float* cx) {
-    const int k = a.k;
+__device__ uint32_t admitted_children(const NGramArgs& a, int a2, int a1, const int* ch, const float* cx, int k) {
     uint32_t live = 0;
     for (int j = 0; j < k; ++j)
         if (cx[j] != -INFINITY) live |= 1u << j;
     if (live == 0) return 0;
     // context ids come from the caller's ctx for the first depths: ids outside
     // [0, V) index no table row and admit nothing
-    const bool bigram = a.ng_kind == DT_NGRAM_DENSE_BIGRAM || a.ng_kind == DT_NGRAM_CSR_BIGRAM;
+    const bool bigram = a.kind == DT_NGRAM_DENSE_BIGRAM || a.kind == DT_NGRAM_CSR_BIGRAM;
     if (bigram && (a1 < 0 || a1 >= a.V)) return 0;
     uint32_t m = 0;
-    if (a.ng_kind == DT_NGRAM_DENSE_BIGRAM) {
+    if (a.kind == DT_NGRAM_DENSE_BIGRAM) {
         const float* row = a.dense + (int64_t)a1 * a.V;
         for (int j = 0; j < k; ++j)
             if (row[ch[j]] > a.min_logp) m |= 1u << j;
-    } else if (a.ng_kind == DT_NGRAM_CSR_BIGRAM) {
+    } else if (a.kind == DT_NGRAM_CSR_BIGRAM) {
         const int lo = a.row_ptr[a1], hi = a.row_ptr[a1 + 1];
         if (hi - lo <= 64) {
             for (int e = lo; e < hi; ++e) {
@@ -280,7 +286,7 @@ __device__ uint32_t admitted_children(const TreeArgs& a, int a2, int a1, const i
                 if (l < hi && a.col[l] == ch[j] && logp_keeps(a, a.csr_logp, l)) m |= 1u << j;
             }
         }
-    } else if (a.ng_kind == DT_NGRAM_HASH_TRIGRAM) {
+    } else if (a.kind == DT_NGRAM_HASH_TRIGRAM) {
         const unsigned long long key = ((unsigned long long)(uint32_t)a2 << 32) | (uint32_t)a1;
         // the successor row of the home slot is read while the key group is
         // probed: a present key usually sits in its home slot
@@ -348,7 +354,14 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
 struct __align__(16) SurvKey {
     double rk;
     uint32_t tie;
-    uint32_t slot;
+    uint32_t j;           // index of the child in T_{t-1}
+};
+// what a winner needs besides its key: cumulative score and the continuity
+// mask of its own children's context
+struct __align__(16) SurvAux {
+    double s;
+    uint32_t cm;
+    uint32_t pad;
 };
 
 template <typename T>
@@ -377,84 +390,84 @@ __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
     return before + x - v;
 }
 
-template <int RM>
-__global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
-    extern __shared__ __align__(16) unsigned char lds[];
-    const TreePlan& P = a.plan;
-    const int b = blockIdx.x;
+// ---------------------------------------------------------------------------
+// prep: rows, continuity and parent-conditioned terms of one depth
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
+    __shared__ unsigned long long s_scratch[kPrepRows][kMergeKeysPerRow + 8];
+    __shared__ int s_tok[kPrepRows][kMaxK];
+    __shared__ float s_x[kPrepRows][kMaxK];
+    __shared__ double s_lse[kPrepRows];
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-    const int d = a.d, k = a.k, W = a.W, budget = a.budget;
-    const int kind = a.ng_kind;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int d = a.d, k = a.k;
+    const int split = blockIdx.x % a.nsplit;
+    const int bt = blockIdx.x / a.nsplit;
+    const int b = bt / d, t = bt - b * d + 1;                  // depth t = 1..d
+    const int kind = a.ng.kind;
     const bool dartree = a.mode == DT_MODE_DARTREE;
-
-    double* s_lse = lds_at<double>(lds, P.off_lse);
-    int* s_ttok = lds_at<int>(lds, P.off_ttok);
-    float* s_tx = lds_at<float>(lds, P.off_tx);
-    uint32_t* s_vmask = lds_at<uint32_t>(lds, P.off_vmask);
-    double* s_g = lds_at<double>(lds, P.off_g);
-    int* n_tok = lds_at<int>(lds, P.off_n_tok);
-    int* n_par = lds_at<int>(lds, P.off_n_par);
-    int* n_dep = lds_at<int>(lds, P.off_n_dep);
-    int* n_tidx = lds_at<int>(lds, P.off_n_tidx);
-    uint32_t* n_cmask = lds_at<uint32_t>(lds, P.off_n_cctx);   // children's continuity mask
-    SurvKey* sv_key = lds_at<SurvKey>(lds, P.off_sv_key);
-    double* sv_s = lds_at<double>(lds, P.off_sv_s);
-    int* n_new = lds_at<int>(lds, P.off_n_new);
-    int* n_out = lds_at<int>(lds, P.off_n_out);
-    double* n_rk = lds_at<double>(lds, P.off_n_rk);
-    double* n_s = lds_at<double>(lds, P.off_n_s);
-    int* misc = lds_at<int>(lds, P.off_misc);
-    unsigned long long* merge = lds_at<unsigned long long>(lds, P.off_merge) +
-                                (wave < kMergeWaves ? wave : 0) * kMergeKeysPerRow;
-
+    const bool trigram = kind == DT_NGRAM_HASH_TRIGRAM;
     const int ctx0 = a.ctx[2 * b], ctx1 = a.ctx[2 * b + 1];
 
-    // ---- 1. normalisers and top-k lists of the d positions
-    if (wave < kMergeWaves)
-        for (int i = wave; i < d; i += kMergeWaves)
-            merge_row(a.part_m, a.part_s, a.part_keys, (int64_t)b * d + i, a.C, k, merge, lane,
-                      &s_lse[i], &s_ttok[i * k], &s_tx[i * k]);
+    // ---- 1. wave w merges row t-1-w: the children (w = 0), the parents'
+    //         tokens (w = 1) and, for the trigram, the grandparents' (w = 2)
+    const int rows = 1 + ((t >= 2 && (kind != DT_NGRAM_NONE || dartree)) ? 1 : 0) + ((t >= 3 && trigram) ? 1 : 0);
+    if (wave < rows) {
+        const int64_t row = (int64_t)b * d + (t - 1 - wave);
+        merge_row(a.part_m, a.part_s, a.part_keys, row, a.L, k, s_scratch[wave], lane, &s_lse[wave],
+                  s_tok[wave], s_x[wave]);
+        if (wave == 0 && split == 0) {                       // row t-1 is written once
+            if (lane < k) {
+                a.ttok[row * k + lane] = s_tok[0][lane];
+                a.tx[row * k + lane] = s_x[0][lane];
+            }
+            if (lane == 0) a.lse[row] = s_lse[0];
+        }
+    }
     __syncthreads();
 
-    // ---- 2a. continuity of every context a parent can have
-    for (int ci = tid; ci < P.n_ctx; ci += kTreeThreads) {
-        int t, a2, a1;
-        if (ci == 0) {
-            t = 1; a2 = ctx0; a1 = ctx1;
-        } else if (kind == DT_NGRAM_HASH_TRIGRAM) {
-            if (ci < 1 + k) {
-                t = 2; a2 = ctx1; a1 = s_ttok[ci - 1];
-            } else {
-                int r = ci - 1 - k;
-                t = 3 + r / (k * k);
-                r -= (t - 3) * k * k;
-                a2 = s_ttok[(t - 3) * k + r / k];
-                a1 = s_ttok[(t - 2) * k + r % k];
-            }
+    // ---- 2. continuity of depth t's contexts against the children T_{t-1}
+    if (kind != DT_NGRAM_NONE) {
+        int n_t, base;                                       // contexts of depth t, index of the first
+        if (t == 1) {
+            n_t = 1;
+            base = 0;
+        } else if (trigram) {
+            n_t = t == 2 ? k : k * k;
+            base = t == 2 ? 1 : 1 + k + (t - 3) * k * k;
         } else {
-            t = 2 + (ci - 1) / k;
-            a2 = 0;
-            a1 = s_ttok[(t - 2) * k + (ci - 1) % k];
+            n_t = k;
+            base = 1 + (t - 2) * k;
         }
-        s_vmask[ci] = admitted_children(a, a2, a1, s_ttok + (t - 1) * k, s_tx + (t - 1) * k);
+        const int per = (n_t + a.nsplit - 1) / a.nsplit;
+        const int lo = split * per, hi = lo + per < n_t ? lo + per : n_t;
+        for (int c = lo + tid; c < hi; c += kThreads) {
+            int a2 = 0, a1;
+            if (t == 1) {
+                a2 = ctx0;
+                a1 = ctx1;
+            } else if (trigram) {
+                a2 = t == 2 ? ctx1 : s_tok[2][c / k];
+                a1 = t == 2 ? s_tok[1][c] : s_tok[1][c % k];
+            } else {
+                a1 = s_tok[1][c];
+            }
+            a.vmask[(int64_t)b * a.n_ctx + base + c] = admitted_children(a.ng, a2, a1, s_tok[0], s_x[0], k);
+        }
     }
 
-    // ---- 2b. DARTree parent-conditioned terms G_t[i][j] = E[par_i] . F[T_{t-1}[j]]
-    //          with par = root token (t = 1) or T_{t-2}; fp64 MFMA 16x16x4 tiles
-    if (dartree) {
+    // ---- 3. DARTree: G_t[i][j] = E[par_i] . F[T_{t-1}[j]], par = root token
+    //         (t = 1) or T_{t-2}; fp64 MFMA 16x16x4 tiles, one per wave
+    if (dartree && split == 0) {
         const int tk = (k + 15) >> 4;
-        const int tiles = d * tk * tk;
-        for (int tile = wave; tile < tiles; tile += kTreeWaves) {
-            const int t = 1 + tile / (tk * tk);
-            const int r = tile - (t - 1) * tk * tk;
-            const int ti = r / tk, tj = r - ti * tk;
-            const int kp = t == 1 ? 1 : k;
-            if (ti * 16 >= kp) continue;                      // wave-uniform
+        const int kp = t == 1 ? 1 : k;
+        const int tiles = ((kp + 15) >> 4) * tk;
+        for (int tile = wave; tile < tiles; tile += kThreads / 64) {
+            const int ti = tile / tk, tj = tile - ti * tk;
             const int i = ti * 16 + (lane & 15), j = tj * 16 + (lane & 15), grp = lane >> 4;
-            int ptok = i < kp ? (t == 1 ? ctx1 : s_ttok[(t - 2) * k + i]) : -1;
-            if (ptok >= a.V) ptok = -1;                           // out-of-range root id: no term
-            const int ctok = j < k ? s_ttok[(t - 1) * k + j] : -1;
+            int ptok = i < kp ? (t == 1 ? ctx1 : s_tok[1][i]) : -1;
+            if (ptok >= a.ng.V) ptok = -1;                         // out-of-range root id: no term
+            const int ctok = j < k ? s_tok[0][j] : -1;
             const float* er = ptok >= 0 ? a.E + (int64_t)ptok * a.R : nullptr;
             const float* fr = ctok >= 0 ? a.F + (int64_t)ctok * a.R : nullptr;
             // The dot product is a sum over the rank index; step q of a block of
@@ -485,24 +498,72 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
                 for (int q = 0; q < 16; ++q)
                     if (q < per) acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ea[q], (double)fb[q], acc, 0, 0, 0);
             }
+            double* gt = a.g + ((int64_t)b * d + (t - 1)) * k * k;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {                          // D[lane/16 + 4q][lane%16]
                 const int ii = ti * 16 + (lane >> 4) + 4 * q, jj = tj * 16 + (lane & 15);
-                if (ii < kp && jj < k) s_g[((t - 1) * k + ii) * k + jj] = acc[q];
+                if (ii < kp && jj < k) gt[ii * k + jj] = acc[q];
             }
         }
     }
+}
+
+template <int RM>
+__global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const TreePlan& P = a.plan;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int d = a.d, k = a.k, W = a.W, budget = a.budget;
+    const int kind = a.ng_kind;
+    const bool dartree = a.mode == DT_MODE_DARTREE;
+
+    double* s_lse = lds_at<double>(lds, P.off_lse);
+    int* s_ttok = lds_at<int>(lds, P.off_ttok);
+    float* s_tx = lds_at<float>(lds, P.off_tx);
+    uint32_t* s_vmask = lds_at<uint32_t>(lds, P.off_vmask);
+    double* s_g = lds_at<double>(lds, P.off_g);
+    int* n_tok = lds_at<int>(lds, P.off_n_tok);
+    int* n_par = lds_at<int>(lds, P.off_n_par);
+    int* n_dep = lds_at<int>(lds, P.off_n_dep);
+    int* n_tidx = lds_at<int>(lds, P.off_n_tidx);
+    uint32_t* n_cmask = lds_at<uint32_t>(lds, P.off_n_cctx);   // children's continuity mask
+    SurvKey* sv_key = lds_at<SurvKey>(lds, P.off_sv_key);
+    SurvAux* sv_aux = lds_at<SurvAux>(lds, P.off_sv_s);
+    int* n_new = lds_at<int>(lds, P.off_n_new);
+    int* n_out = lds_at<int>(lds, P.off_n_out);
+    double* n_rk = lds_at<double>(lds, P.off_n_rk);
+    double* n_s = lds_at<double>(lds, P.off_n_s);
+    int* misc = lds_at<int>(lds, P.off_misc);
+    // ---- load what the prep kernel derived for this request (contiguous)
+    {
+        const int64_t r0 = (int64_t)b * d;
+        for (int i = tid; i < d; i += kTreeThreads) s_lse[i] = a.lse[r0 + i];
+        for (int i = tid; i < d * k; i += kTreeThreads) {
+            s_ttok[i] = a.ttok[r0 * k + i];
+            s_tx[i] = a.tx[r0 * k + i];
+        }
+        for (int i = tid; i < P.n_ctx; i += kTreeThreads) s_vmask[i] = a.vmask[(int64_t)b * a.n_ctx + i];
+        if (dartree)
+            for (int i = tid; i < d * k * k; i += kTreeThreads) s_g[i] = a.g[r0 * k * k + i];
+    }
     __syncthreads();
 
-    // ---- 3. depth loop, run by wave 0 alone (wave-synchronous, no barriers).
-    //      Candidate keys go to registers (slot r*64 + lane, slot =
-    //      parent_rank * k + child).  With a full frontier only candidates whose
-    //      key reaches the smallest "first valid child" key of the W rows can be
-    //      among the top W (those W candidates are distinct); the survivors are
-    //      packed into LDS and every lane ranks its own survivor by streaming
-    //      all of them, so the winners are written in parallel.
+    // ---- 4. depth loop, run by wave 0 alone (wave-synchronous, no barriers).
+    //      Candidate slot r*64 + lane = parent_rank * k + child.  Every phase
+    //      issues its LDS reads together, so a depth costs about three LDS
+    //      round trips: (a) the candidates read the child's logit and token
+    //      and the parent's record; (b) the candidates that can still win fetch
+    //      the continuity mask of their own children's context and are packed
+    //      (with a full frontier only keys that reach the smallest "first valid
+    //      child" key of the W parents can be among the top W: those W
+    //      candidates are distinct); (c) every lane ranks one survivor by
+    //      streaming all of them, sixteen per step, and the winners write
+    //      their node records in parallel.
     int nb = 0;       // nodes in the candidate tree
     if (wave == 0) {
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
         int f = 1;        // frontier size (depth 0: the root)
         int fbase = 0;    // BFS index of the first frontier node
         const uint32_t root_mask = kind == DT_NGRAM_NONE ? 0xFFFFFFFFu : s_vmask[0];
@@ -516,57 +577,73 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
         for (int t = 1; t <= d; ++t) {
             const int tk = (t - 1) * k;
             const int m = f * k;
-            const int R = (m + 63) >> 6;
             const double lse_t = readlane_d(lse_l, t - 1);
             const uint32_t live = (uint32_t)__builtin_amdgcn_readlane((int)live_l, t - 1);
+            const bool next_ctx = kind != DT_NGRAM_NONE && t < d;
+            // (a) one batch of LDS reads for all rounds; indices are clamped so
+            //     every read is in bounds and no read waits on a branch
+            int cj[RM], cp[RM], ctok[RM], cgp[RM];
+            uint32_t ccm[RM];
+            float cx[RM];
+            double cprk[RM], cps[RM];
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                const int slot = r * 64 + lane;
+                const int sl = slot < m ? slot : 0;
+                const int p = (int)(((float)sl + 0.5f) * inv_k);    // exact: slot < 2^11
+                const int j = sl - p * k;
+                const int nd = t > 1 ? fbase + p : 0;
+                cj[r] = j;
+                cp[r] = p;
+                cx[r] = s_tx[tk + j];
+                ctok[r] = s_ttok[tk + j];
+                ccm[r] = n_cmask[nd];
+                cprk[r] = n_rk[nd];
+                cps[r] = n_s[nd];
+                cgp[r] = n_tidx[nd];
+            }
             double krk[RM], ksc[RM];
             uint32_t ktie[RM];
-            int kgp[RM];
             bool kok[RM];
             int nvalid = 0, nfirst = 0;
             double firstmin = INFINITY;
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
                 const int slot = r * 64 + lane;
-                bool ok = false, first = false;
-                krk[r] = -INFINITY;
-                ksc[r] = -INFINITY;
-                ktie[r] = 0xFFFFFFFFu;
-                kgp[r] = 0;
-                if (r < R && slot < m) {
-                    const int p = (int)(((float)slot + 0.5f) * inv_k);   // exact: slot < 2^11
-                    const int j = slot - p * k;
-                    const float x = s_tx[tk + j];
-                    uint32_t cm = root_mask;
-                    double prk = 0.0, ps = 0.0;
-                    int gp = 0;
-                    if (t > 1) {
-                        const int nd = fbase + p;
-                        cm = n_cmask[nd];
-                        prk = n_rk[nd];
-                        ps = n_s[nd];
-                        gp = n_tidx[nd];
-                    }
-                    kgp[r] = gp;
-                    const uint32_t rowv = cm & live;
-                    ok = (rowv >> j) & 1u;
-                    first = ok && j == __builtin_ctz(rowv);
-                    if (ok) {
-                        const double g = dartree ? s_g[(tk + gp) * k + j] : 0.0;
-                        krk[r] = (prk + (double)x) + g;
-                        ksc[r] = (ps + ((double)x - lse_t)) + g;
-                        ktie[r] = ((uint32_t)s_ttok[tk + j] << 6) | (uint32_t)p;
-                        if (first) firstmin = fmin(firstmin, krk[r]);
-                    }
+                const int j = cj[r];
+                uint32_t cm = root_mask;
+                double prk = 0.0, ps = 0.0;
+                if (t > 1) {
+                    cm = ccm[r];
+                    prk = cprk[r];
+                    ps = cps[r];
                 }
+                const uint32_t rowv = cm & live;
+                const bool ok = slot < m && ((rowv >> j) & 1u);
+                const bool first = ok && j == __builtin_ctz(rowv);
+                const double g = (dartree && ok) ? s_g[(tk + (t > 1 ? cgp[r] : 0)) * k + j] : 0.0;
+                krk[r] = ok ? (prk + (double)cx[r]) + g : -INFINITY;
+                ksc[r] = ok ? (ps + ((double)cx[r] - lse_t)) + g : -INFINITY;
+                ktie[r] = ok ? (((uint32_t)ctok[r] << 6) | (uint32_t)cp[r]) : 0xFFFFFFFFu;
+                if (first) firstmin = fmin(firstmin, krk[r]);
                 kok[r] = ok;
                 nvalid += __popcll(__ballot(ok));
                 nfirst += __popcll(__ballot(first));
             }
             if (nvalid == 0) break;
             const int keep = nvalid < W ? nvalid : W;
+            // (b) survivors, each with the continuity mask of its children's
+            //     context (fetched before the reduction, so the two overlap)
+            uint32_t kcm[RM];
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                kcm[r] = 0xFFFFFFFFu;
+                if (next_ctx) {
+                    const int ci = kok[r] ? ctx_index(kind, k, t + 1, t == 1 ? 0 : cgp[r], cj[r]) : 0;
+                    kcm[r] = s_vmask[ci];
+                }
+            }
             const double lb = nfirst >= W ? __ockl_wfred_min_f64(firstmin) : -INFINITY;
-            // pack the survivors
             int ns = 0;
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
@@ -574,47 +651,42 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
                 const unsigned long long bal = __ballot(in);
                 if (in) {
                     const int e = ns + lanes_below(bal);
-                    sv_key[e] = SurvKey{krk[r], ktie[r], (uint32_t)(r * 64 + lane) | ((uint32_t)kgp[r] << 16)};
-                    sv_s[e] = ksc[r];
+                    sv_key[e] = SurvKey{krk[r], ktie[r], (uint32_t)cj[r]};
+                    sv_aux[e] = SurvAux{ksc[r], kcm[r], 0u};
                 }
                 ns += __popcll(bal);
             }
+            // sentinels (Rk = -inf beats nothing) round the list up to a
+            // multiple of sixteen
+            const int ns16 = (ns + 15) & ~15;
+            if (lane < ns16 - ns) sv_key[ns + lane] = SurvKey{-INFINITY, 0xFFFFFFFFu, 0u};
             __builtin_amdgcn_wave_barrier();
-            // rank: lane e holds survivor e (blocks of 64); all others stream past it
+            // (c) rank: lane e holds survivor e (blocks of 64)
             for (int e0 = 0; e0 < ns; e0 += 64) {
                 const int e = e0 + lane;
-                SurvKey me{-INFINITY, 0xFFFFFFFFu, 0u};
-                if (e < ns) me = sv_key[e];
+                const int ec = e < ns ? e : 0;
+                const SurvKey me = sv_key[ec];
+                const SurvAux ax = sv_aux[ec];
                 int rank = 0;
-                int q = 0;
-                for (; q + 8 <= ns; q += 8) {            // eight independent LDS reads per step
-                    SurvKey o[8];
+                for (int q = 0; q < ns16; q += 16) {
+                    u4 o[16];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) o[u] = sv_key[q + u];
+                    for (int u = 0; u < 16; ++u) o[u] = *reinterpret_cast<const u4*>(&sv_key[q + u]);
 #pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        rank += (o[u].rk > me.rk) | ((o[u].rk == me.rk) & (o[u].tie < me.tie));
-                }
-                for (; q < ns; ++q) {
-                    const SurvKey o = sv_key[q];
-                    rank += (o.rk > me.rk) | ((o.rk == me.rk) & (o.tie < me.tie));
+                    for (int u = 0; u < 16; ++u) {
+                        const double ork = __longlong_as_double(((long long)o[u].y << 32) | o[u].x);
+                        rank += (ork > me.rk) | ((ork == me.rk) & (o[u].z < me.tie));
+                    }
                 }
                 if (e < ns && rank < keep) {
-                    const int slot = (int)(me.slot & 0xFFFFu);
-                    const int pj = (int)(me.slot >> 16);          // parent's index in T_{t-2}
-                    const int p = (int)(me.tie & 63u);
-                    const int j = slot - p * k;
                     const int nd = nb + rank;
-                    uint32_t cm = 0xFFFFFFFFu;
-                    if (kind != DT_NGRAM_NONE && t < d) cm = s_vmask[ctx_index(kind, k, t + 1, t == 1 ? 0 : pj, j)];
-                    const double sc = sv_s[e];
                     n_tok[nd] = (int)(me.tie >> 6);
-                    n_par[nd] = t == 1 ? -1 : fbase + p;
+                    n_par[nd] = t == 1 ? -1 : fbase + (int)(me.tie & 63u);
                     n_dep[nd] = t;
-                    n_tidx[nd] = j;
+                    n_tidx[nd] = (int)me.j;
                     n_rk[nd] = me.rk;
-                    n_s[nd] = sc;
-                    n_cmask[nd] = cm;
+                    n_s[nd] = ax.s;
+                    n_cmask[nd] = ax.cm;
                 }
             }
             __builtin_amdgcn_wave_barrier();
@@ -627,7 +699,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     __syncthreads();
     nb = *(volatile int*)&misc[0];
 
-    // ---- 4. verification budget
+    // ---- 5. verification budget
     int n_sel = nb;
     if (nb <= budget) {
         for (int i = tid; i < nb; i += kTreeThreads) {
@@ -725,7 +797,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
         __syncthreads();
     }
 
-    // ---- 5. outputs in BFS order, parents remapped, ancestor mask
+    // ---- 6. outputs in BFS order, parents remapped, ancestor mask
     const int64_t ob = (int64_t)b * budget;
     for (int o = tid; o < budget; o += kTreeThreads) {
         if (o < n_sel) {
@@ -758,7 +830,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
 
 // one wave per row: per-position normaliser and top-k only
 __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
-    __shared__ unsigned long long scratch[kWaves][kMergeKeysPerRow];
+    __shared__ unsigned long long scratch[kWaves][kMergeKeysPerRow + 8];
     __shared__ int s_tok[kWaves][kMaxK];
     __shared__ float s_val[kWaves][kMaxK];
     __shared__ double s_lse[kWaves];
@@ -775,6 +847,13 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
 }
 
 }  // namespace
+
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
+    if (a.B <= 0) return hipSuccess;
+    const int64_t grid = (int64_t)a.B * a.d * a.nsplit;
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_tree(const TreeArgs& a, hipStream_t stream) {
     if (a.B <= 0) return hipSuccess;
