@@ -319,6 +319,103 @@ __device__ uint32_t admitted_children(const NGramArgs& a, int a2, int a1, const 
     return m & live;
 }
 
+// Children of one depth by token: an open-addressing table in LDS
+// (kChildSlots slots, load <= 1/4) maps a token to its index in T_{t-1}.
+constexpr int kChildSlots = 128;
+__device__ __forceinline__ uint32_t child_hash(int tok) { return ((uint32_t)tok * 2654435761u) >> 25; }
+
+// Index in T_{t-1} of token s, or -1.
+__device__ __forceinline__ int child_index(const int* ctok, const int* cj, int s) {
+    if (s < 0) return -1;
+    uint32_t pos = child_hash(s);
+    for (int probe = 0; probe < kChildSlots; ++probe) {
+        const int t = ctok[pos];
+        if (t == s) return cj[pos];
+        if (t == -1) return -1;
+        pos = (pos + 1) & (kChildSlots - 1);
+    }
+    return -1;
+}
+
+// OR over the four lanes of a quad (DPP quad permutations, no LDS traffic)
+__device__ __forceinline__ uint32_t quad_or(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    return v;
+}
+
+// Successors 4g .. 4g+3 of a 16-wide chunk of a row (-1 past its end):
+// one 16-byte load when the row allows it.
+__device__ __forceinline__ void load_succ4(int (&r)[4], const int* row, int from, int n) {
+    typedef int i4 __attribute__((ext_vector_type(4)));
+    const int* p = row + from;
+    if (from + 4 <= n && ((uintptr_t)p & 15u) == 0) {
+        const i4 x = *reinterpret_cast<const i4*>(p);
+        r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = from + u < n ? p[u] : -1;
+    }
+}
+
+// Admissible children of the trigram context (a2, a1), computed by the four
+// lanes of a quad together (g = lane & 3): lane g probes slots 2g and 2g+1 of
+// every window of 8 probe positions and holds successors 4g..4g+3 of every 16
+// of the row, and each successor is mapped to its child index through the
+// LDS table.  The first window and the home slot's row are read at once, so a
+// key found in its home slot costs one memory round trip.  Inactive quads
+// (`active` false in all four lanes) read in bounds and return 0.  The
+// result is the same in all four lanes.
+__device__ uint32_t quad_admitted(const NGramArgs& a, int a2, int a1, bool active, int g,
+                                  const int* ctok, const int* cj, uint32_t live) {
+    const unsigned long long key = ((unsigned long long)(uint32_t)a2 << 32) | (uint32_t)a1;
+    const long long cm = a.cap - 1;
+    const long long home = active ? (long long)(mix64(key) & (unsigned long long)cm) : 0;
+    const int S = a.S;
+    // trip 1: probe window 0 and the first 16 successors of the home slot
+    unsigned long long k0 = a.keys[(home + 2 * g) & cm], k1 = a.keys[(home + 2 * g + 1) & cm];
+    int spec[4];
+    load_succ4(spec, a.succ + home * S, 4 * g, S);
+    long long slot = -1;
+    bool done = !active;
+    for (long long w0 = 0; !done; w0 += 8) {
+        if (w0 > 0) {
+            k0 = a.keys[(home + w0 + 2 * g) & cm];
+            k1 = a.keys[(home + w0 + 2 * g + 1) & cm];
+        }
+        // probe order within the window: slot 2g + e of lane g
+        const uint32_t hitm = (uint32_t)(k0 == key) | ((uint32_t)(k1 == key) << 1);
+        const uint32_t endm = hitm | (uint32_t)(k0 == kEmptyKey) | ((uint32_t)(k1 == kEmptyKey) << 1);
+        const uint32_t F = quad_or(endm << (2 * g)), M = quad_or(hitm << (2 * g));
+        if (F != 0u) {
+            const int idx = __builtin_ctz(F);
+            if ((M >> idx) & 1u) slot = (home + w0 + idx) & cm;
+            done = true;
+        } else if (w0 + 8 >= a.cap) {
+            done = true;                                      // every slot seen: absent
+        }
+    }
+    if (slot < 0) return 0u;
+    const bool membership = a.min_logp == -INFINITY || a.hash_logp == nullptr;
+    const int* row = a.succ + slot * S;
+    uint32_t hit = 0;
+    for (int c0 = 0; c0 < S; c0 += 16) {
+        int sv[4];
+        if (c0 == 0 && slot == home) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sv[u] = spec[u];
+        } else {
+            load_succ4(sv, row, c0 + 4 * g, S);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = child_index(ctok, cj, sv[u]);
+            if (j >= 0 && (membership || a.hash_logp[slot * S + c0 + 4 * g + u] > a.min_logp)) hit |= 1u << j;
+        }
+    }
+    return quad_or(hit) & live;
+}
+
 // Index of a continuity context.  Depth t's contexts: bigram -> parent token
 // (t = 1: the root; t >= 2: T_{t-2}[i1]); trigram -> (grandparent, parent)
 // (t = 1: (ctx0, ctx1); t = 2: (ctx1, T_0[i1]); t >= 3: (T_{t-3}[i2], T_{t-2}[i1])).
@@ -398,6 +495,8 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
     __shared__ int s_tok[kPrepRows][kMaxK];
     __shared__ float s_x[kPrepRows][kMaxK];
     __shared__ double s_lse[kPrepRows];
+    __shared__ int s_ctok[kChildSlots];
+    __shared__ int s_cj[kChildSlots];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int d = a.d, k = a.k;
@@ -441,18 +540,46 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
         }
         const int per = (n_t + a.nsplit - 1) / a.nsplit;
         const int lo = split * per, hi = lo + per < n_t ? lo + per : n_t;
-        for (int c = lo + tid; c < hi; c += kThreads) {
-            int a2 = 0, a1;
-            if (t == 1) {
-                a2 = ctx0;
-                a1 = ctx1;
-            } else if (trigram) {
-                a2 = t == 2 ? ctx1 : s_tok[2][c / k];
-                a1 = t == 2 ? s_tok[1][c] : s_tok[1][c % k];
-            } else {
-                a1 = s_tok[1][c];
+        if (trigram) {
+            // children of depth t by token, then one quad per context
+            for (int i = tid; i < kChildSlots; i += kThreads) s_ctok[i] = -1;
+            __syncthreads();
+            if (tid < k) {
+                const int tok = s_tok[0][tid];
+                uint32_t pos = child_hash(tok);
+                while (true) {                               // <= 32 keys in 128 slots
+                    if (atomicCAS(&s_ctok[pos], -1, tok) == -1) {
+                        s_cj[pos] = tid;
+                        break;
+                    }
+                    pos = (pos + 1) & (kChildSlots - 1);
+                }
             }
-            a.vmask[(int64_t)b * a.n_ctx + base + c] = admitted_children(a.ng, a2, a1, s_tok[0], s_x[0], k);
+            __syncthreads();
+            uint32_t live = 0;
+            for (int j = 0; j < k; ++j) live |= (uint32_t)(s_x[0][j] != -INFINITY) << j;
+            const int g = tid & 3;
+            for (int c0 = lo; c0 < hi; c0 += kThreads / 4) {
+                const int c = c0 + (tid >> 2);
+                const bool active = c < hi;
+                int a2 = 0, a1 = 0;
+                if (active) {
+                    if (t == 1) {
+                        a2 = ctx0;
+                        a1 = ctx1;
+                    } else {
+                        a2 = t == 2 ? ctx1 : s_tok[2][c / k];
+                        a1 = t == 2 ? s_tok[1][c] : s_tok[1][c % k];
+                    }
+                }
+                const uint32_t m = quad_admitted(a.ng, a2, a1, active, g, s_ctok, s_cj, live);
+                if (active && g == 0) a.vmask[(int64_t)b * a.n_ctx + base + c] = m;
+            }
+        } else {
+            for (int c = lo + tid; c < hi; c += kThreads) {
+                const int a1 = t == 1 ? ctx1 : s_tok[1][c];
+                a.vmask[(int64_t)b * a.n_ctx + base + c] = admitted_children(a.ng, 0, a1, s_tok[0], s_x[0], k);
+            }
         }
     }
 
