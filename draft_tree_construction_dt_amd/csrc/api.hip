@@ -82,16 +82,14 @@ TreePlan plan_tree(const dt_params* p, int kind) {
     P.off_tx = take(d * k * 4, 4);
     P.off_vmask = take(P.n_ctx * 4, 4);
     P.off_misc = take(kMiscInts * 4, 4);
-    P.off_sv_key = take((P.max_cand + 16) * 16, 16);  // + a block of sentinels
-    P.off_sv_s = take((P.max_cand + 16) * 16, 16);
+    P.off_sv_key = take((P.max_cand + 32) * 16, 16);  // + a block of sentinels
+    P.off_sv_s = take((P.max_cand + 32) * 16, 16);
     const int nn = P.max_nodes;
-    P.off_n_rk = take(nn * 8, 8);
+    P.off_n_rec = take(nn * 32, 16);
     P.off_n_s = take(nn * 8, 8);
     P.off_n_tok = take(nn * 4, 4);
     P.off_n_par = take(nn * 4, 4);
     P.off_n_dep = take(nn * 4, 4);
-    P.off_n_tidx = take(nn * 4, 4);
-    P.off_n_cctx = take(nn * 4, 4);
     P.off_n_new = take(nn * 4, 4);
     P.off_n_out = take(nn * 4, 4);
     P.total = (int)round_up(off, 16);

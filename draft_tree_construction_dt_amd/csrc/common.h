@@ -78,10 +78,10 @@ struct TreePlan {
     int off_tx;         // float  [d][k]   their logits
     int off_vmask;      // uint32 [n_ctx]  admissible children (bit j = T[t-1][j])
     int off_g;          // double [d][k][k] parent-conditioned terms (DARTree)
-    int off_n_tok, off_n_par, off_n_dep, off_n_tidx, off_n_cctx, off_n_new, off_n_out;
-    int off_n_rk, off_n_s;
-    int off_sv_key;     // 16-byte survivor keys [W*k + 16] of the depth loop
-    int off_sv_s;       // 16-byte survivor records [W*k + 16]: score and children's mask
+    int off_n_tok, off_n_par, off_n_dep, off_n_new, off_n_out, off_n_s;
+    int off_n_rec;      // 32-byte frontier records [d*W] read by the next depth
+    int off_sv_key;     // 16-byte survivor keys [W*k + 32] of the depth loop
+    int off_sv_s;       // 16-byte survivor records [W*k + 32]: score and children's mask
     int off_misc;       // int counters
     int total;
 };

@@ -460,6 +460,14 @@ struct __align__(16) SurvAux {
     uint32_t cm;
     uint32_t pad;
 };
+// a frontier node as the next depth reads it: key, score, the continuity
+// mask of its children's context and its index in its own T list
+struct __align__(16) NodeRec {
+    double rk;
+    double s;
+    uint32_t cm;
+    uint32_t tidx;
+};
 
 template <typename T>
 __device__ __forceinline__ T* lds_at(unsigned char* base, int off) {
@@ -654,13 +662,11 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     int* n_tok = lds_at<int>(lds, P.off_n_tok);
     int* n_par = lds_at<int>(lds, P.off_n_par);
     int* n_dep = lds_at<int>(lds, P.off_n_dep);
-    int* n_tidx = lds_at<int>(lds, P.off_n_tidx);
-    uint32_t* n_cmask = lds_at<uint32_t>(lds, P.off_n_cctx);   // children's continuity mask
+    NodeRec* n_rec = lds_at<NodeRec>(lds, P.off_n_rec);
     SurvKey* sv_key = lds_at<SurvKey>(lds, P.off_sv_key);
     SurvAux* sv_aux = lds_at<SurvAux>(lds, P.off_sv_s);
     int* n_new = lds_at<int>(lds, P.off_n_new);
     int* n_out = lds_at<int>(lds, P.off_n_out);
-    double* n_rk = lds_at<double>(lds, P.off_n_rk);
     double* n_s = lds_at<double>(lds, P.off_n_s);
     int* misc = lds_at<int>(lds, P.off_misc);
     // ---- load what the prep kernel derived for this request (contiguous)
@@ -679,18 +685,21 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
 
     // ---- 4. depth loop, run by wave 0 alone (wave-synchronous, no barriers).
     //      Candidate slot r*64 + lane = parent_rank * k + child.  Every phase
-    //      issues its LDS reads together, so a depth costs about three LDS
-    //      round trips: (a) the candidates read the child's logit and token
-    //      and the parent's record; (b) the candidates that can still win fetch
-    //      the continuity mask of their own children's context and are packed
-    //      (with a full frontier only keys that reach the smallest "first valid
-    //      child" key of the W parents can be among the top W: those W
-    //      candidates are distinct); (c) every lane ranks one survivor by
-    //      streaming all of them, sixteen per step, and the winners write
-    //      their node records in parallel.
+    //      issues its LDS reads together, so a depth costs a few LDS round
+    //      trips: (a) the candidates read the child's logit and token and
+    //      the parent's 32-byte frontier record; (b) the candidates that can
+    //      still win fetch the continuity mask of their own children's
+    //      context and are packed (with a full frontier only keys that reach
+    //      the smallest "first valid child" key of the W parents can be among
+    //      the top W: those W candidates are distinct); (c) ranks among the
+    //      survivors: up to 32 of them are compared all-pairs, each lane
+    //      taking a few rotations of a replicated copy and the replicas'
+    //      counts summed with lane shuffles; more are streamed sixteen at a
+    //      time.  Winners write their records in parallel.
     int nb = 0;       // nodes in the candidate tree
     if (wave == 0) {
         typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
         int f = 1;        // frontier size (depth 0: the root)
         int fbase = 0;    // BFS index of the first frontier node
         const uint32_t root_mask = kind == DT_NGRAM_NONE ? 0xFFFFFFFFu : s_vmask[0];
@@ -701,6 +710,15 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
         uint32_t live_l = 0;
         if (lane < d)
             for (int j = 0; j < k; ++j) live_l |= (uint32_t)(s_tx[lane * k + j] != -INFINITY) << j;
+        // a lane's candidate slots have fixed (parent rank, child) pairs
+        int cj[RM], cp[RM];
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            const int slot = r * 64 + lane;
+            const int sl = slot < kMaxCandidates ? slot : 0;
+            cp[r] = (int)(((float)sl + 0.5f) * inv_k);         // exact: slot < 2^11
+            cj[r] = sl - cp[r] * k;
+        }
         for (int t = 1; t <= d; ++t) {
             const int tk = (t - 1) * k;
             const int m = f * k;
@@ -709,46 +727,37 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
             const bool next_ctx = kind != DT_NGRAM_NONE && t < d;
             // (a) one batch of LDS reads for all rounds; indices are clamped so
             //     every read is in bounds and no read waits on a branch
-            int cj[RM], cp[RM], ctok[RM], cgp[RM];
-            uint32_t ccm[RM];
+            int ctok[RM];
             float cx[RM];
-            double cprk[RM], cps[RM];
+            u4 crec[RM];
+            u2 crec2[RM];
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
-                const int slot = r * 64 + lane;
-                const int sl = slot < m ? slot : 0;
-                const int p = (int)(((float)sl + 0.5f) * inv_k);    // exact: slot < 2^11
-                const int j = sl - p * k;
-                const int nd = t > 1 ? fbase + p : 0;
-                cj[r] = j;
-                cp[r] = p;
-                cx[r] = s_tx[tk + j];
-                ctok[r] = s_ttok[tk + j];
-                ccm[r] = n_cmask[nd];
-                cprk[r] = n_rk[nd];
-                cps[r] = n_s[nd];
-                cgp[r] = n_tidx[nd];
+                const int nd = (t > 1 && r * 64 + lane < m) ? fbase + cp[r] : 0;
+                cx[r] = s_tx[tk + cj[r]];
+                ctok[r] = s_ttok[tk + cj[r]];
+                crec[r] = *reinterpret_cast<const u4*>(&n_rec[nd]);
+                crec2[r] = *reinterpret_cast<const u2*>(&n_rec[nd].cm);
             }
             double krk[RM], ksc[RM];
             uint32_t ktie[RM];
             bool kok[RM];
+            int kgp[RM];
             int nvalid = 0, nfirst = 0;
             double firstmin = INFINITY;
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
                 const int slot = r * 64 + lane;
                 const int j = cj[r];
-                uint32_t cm = root_mask;
-                double prk = 0.0, ps = 0.0;
-                if (t > 1) {
-                    cm = ccm[r];
-                    prk = cprk[r];
-                    ps = cps[r];
-                }
+                const bool root = t == 1;
+                const double prk = root ? 0.0 : __longlong_as_double(((long long)crec[r].y << 32) | crec[r].x);
+                const double ps = root ? 0.0 : __longlong_as_double(((long long)crec[r].w << 32) | crec[r].z);
+                const uint32_t cm = root ? root_mask : crec2[r].x;
+                kgp[r] = root ? 0 : (int)crec2[r].y;
                 const uint32_t rowv = cm & live;
                 const bool ok = slot < m && ((rowv >> j) & 1u);
                 const bool first = ok && j == __builtin_ctz(rowv);
-                const double g = (dartree && ok) ? s_g[(tk + (t > 1 ? cgp[r] : 0)) * k + j] : 0.0;
+                const double g = (dartree && ok) ? s_g[(tk + kgp[r]) * k + j] : 0.0;
                 krk[r] = ok ? (prk + (double)cx[r]) + g : -INFINITY;
                 ksc[r] = ok ? (ps + ((double)cx[r] - lse_t)) + g : -INFINITY;
                 ktie[r] = ok ? (((uint32_t)ctok[r] << 6) | (uint32_t)cp[r]) : 0xFFFFFFFFu;
@@ -760,13 +769,13 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
             if (nvalid == 0) break;
             const int keep = nvalid < W ? nvalid : W;
             // (b) survivors, each with the continuity mask of its children's
-            //     context (fetched before the reduction, so the two overlap)
+            //     context (read before the reduction, so the two overlap)
             uint32_t kcm[RM];
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
                 kcm[r] = 0xFFFFFFFFu;
                 if (next_ctx) {
-                    const int ci = kok[r] ? ctx_index(kind, k, t + 1, t == 1 ? 0 : cgp[r], cj[r]) : 0;
+                    const int ci = kok[r] ? ctx_index(kind, k, t + 1, t == 1 ? 0 : kgp[r], cj[r]) : 0;
                     kcm[r] = s_vmask[ci];
                 }
             }
@@ -784,36 +793,70 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
                 ns += __popcll(bal);
             }
             // sentinels (Rk = -inf beats nothing) round the list up to a
-            // multiple of sixteen
-            const int ns16 = (ns + 15) & ~15;
-            if (lane < ns16 - ns) sv_key[ns + lane] = SurvKey{-INFINITY, 0xFFFFFFFFu, 0u};
+            // multiple of 32
+            const int ns32 = (ns + 31) & ~31;
+            if (lane < ns32 - ns) sv_key[ns + lane] = SurvKey{-INFINITY, 0xFFFFFFFFu, 0u};
             __builtin_amdgcn_wave_barrier();
-            // (c) rank: lane e holds survivor e (blocks of 64)
-            for (int e0 = 0; e0 < ns; e0 += 64) {
-                const int e = e0 + lane;
-                const int ec = e < ns ? e : 0;
-                const SurvKey me = sv_key[ec];
-                const SurvAux ax = sv_aux[ec];
-                int rank = 0;
-                for (int q = 0; q < ns16; q += 16) {
-                    u4 o[16];
+            // (c) ranks
+            if (ns <= 32) {
+                // G lanes per replica, 64/G replicas; lane (rep, i) compares
+                // survivor i with survivors i+s (mod G), s = 1 + rep + u*64/G
+                const int G = ns <= 16 ? 16 : 32;
+                const int F = 64 / G;
+                const int i = lane & (G - 1), rep = lane / G;
+                const SurvKey me = sv_key[i];
+                const SurvAux ax = sv_aux[i];
+                int part = 0;
+                for (int s0 = 1 + rep; s0 < G; s0 += 4 * F) {
+                    u4 o[4];
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) o[u] = *reinterpret_cast<const u4*>(&sv_key[q + u]);
+                    for (int u = 0; u < 4; ++u) {
+                        const int sh = s0 + u * F;
+                        o[u] = *reinterpret_cast<const u4*>(&sv_key[(i + (sh < G ? sh : 0)) & (G - 1)]);
+                    }
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) {
+                    for (int u = 0; u < 4; ++u) {
+                        const int sh = s0 + u * F;
                         const double ork = __longlong_as_double(((long long)o[u].y << 32) | o[u].x);
-                        rank += (ork > me.rk) | ((ork == me.rk) & (o[u].z < me.tie));
+                        part += (sh < G) & ((ork > me.rk) | ((ork == me.rk) & (o[u].z < me.tie)));
                     }
                 }
-                if (e < ns && rank < keep) {
-                    const int nd = nb + rank;
+                if (G == 16) part += __shfl_xor(part, 16);
+                part += __shfl_xor(part, 32);
+                if (rep == 0 && i < ns && part < keep) {
+                    const int nd = nb + part;
                     n_tok[nd] = (int)(me.tie >> 6);
                     n_par[nd] = t == 1 ? -1 : fbase + (int)(me.tie & 63u);
                     n_dep[nd] = t;
-                    n_tidx[nd] = (int)me.j;
-                    n_rk[nd] = me.rk;
                     n_s[nd] = ax.s;
-                    n_cmask[nd] = ax.cm;
+                    n_rec[nd] = NodeRec{me.rk, ax.s, ax.cm, me.j};
+                }
+            } else {
+                // lane e holds survivor e (blocks of 64) and streams past all
+                for (int e0 = 0; e0 < ns; e0 += 64) {
+                    const int e = e0 + lane;
+                    const int ec = e < ns ? e : 0;
+                    const SurvKey me = sv_key[ec];
+                    const SurvAux ax = sv_aux[ec];
+                    int rank = 0;
+                    for (int q = 0; q < ns32; q += 16) {
+                        u4 o[16];
+#pragma unroll
+                        for (int u = 0; u < 16; ++u) o[u] = *reinterpret_cast<const u4*>(&sv_key[q + u]);
+#pragma unroll
+                        for (int u = 0; u < 16; ++u) {
+                            const double ork = __longlong_as_double(((long long)o[u].y << 32) | o[u].x);
+                            rank += (ork > me.rk) | ((ork == me.rk) & (o[u].z < me.tie));
+                        }
+                    }
+                    if (e < ns && rank < keep) {
+                        const int nd = nb + rank;
+                        n_tok[nd] = (int)(me.tie >> 6);
+                        n_par[nd] = t == 1 ? -1 : fbase + (int)(me.tie & 63u);
+                        n_dep[nd] = t;
+                        n_s[nd] = ax.s;
+                        n_rec[nd] = NodeRec{me.rk, ax.s, ax.cm, me.j};
+                    }
                 }
             }
             __builtin_amdgcn_wave_barrier();
