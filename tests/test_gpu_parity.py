@@ -201,6 +201,29 @@ def test_dartree_budget_binding(device, oracle_lib):
         _parity(p, device, oracle_lib, label=f"dartree budget trial {trial}")
 
 
+def test_hash_wide_rows_large_k_and_many_survivors(device, oracle_lib):
+    """Trigram rows longer than 16 successors (several chunks per lookup),
+    row lengths that are not a multiple of four, a 4-slot table whose probe
+    window wraps, k up to 32 (the children's token table full to its bound,
+    contexts split over several workgroups) and frontiers whose survivors
+    exceed 32 (the streamed ranking)."""
+    rng = np.random.default_rng(31)
+    cases = [(20, 17, 1024, 64), (32, 24, 512, 64), (32, 64, 2048, 64), (12, 33, 4, 40), (17, 5, 64, 48)]
+    for i, (k, S, cap, V) in enumerate(cases):
+        W = int(rng.integers(4, 1024 // k + 1))
+        W = min(W, 32)
+        d = int(rng.integers(3, 6))
+        p = synth.random_problem(
+            rng, B=2, V=V, d=d, k=k, W=W, budget=d * W, ngram=NGRAM_HASH_TRIGRAM, density=0.5,
+            hash_cap=cap, hash_S=S, min_logp=-1.0 if i % 2 else -math.inf,
+            dtype=synth.DTYPE_BF16 if i % 2 else synth.DTYPE_F32)
+        _parity(p, device, oracle_lib, label=f"hash k={k} S={S} cap={cap} W={W}")
+    for W, k in [(32, 32), (64, 16)]:
+        p = synth.random_problem(rng, B=2, V=300, d=4, k=k, W=W, budget=min(4 * W, 1024),
+                                 integer_logits=True)
+        _parity(p, device, oracle_lib, label=f"no table W={W} k={k}")
+
+
 def test_zero_requests(device):
     import torch
     from draft_tree_construction_dt_amd import binding as bd
