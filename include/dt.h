@@ -172,8 +172,11 @@ dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngram,
                         const dt_params* params, const dt_tree_out* out);
 
 /* Bytes of workspace dt_build_tree / dt_position_topk need for these
- * parameters (depends on B, V, d, k, dtype and sweep_chunks only); 0 if the
- * parameters are invalid. */
+ * parameters (depends on B, V, d, k, mode, dtype and sweep_chunks only; the
+ * N-gram area is sized for the largest table kind); 0 if the parameters are
+ * invalid.  The workspace holds the sweep's per-chunk partials and the
+ * per-row normalisers, top-k lists, continuity masks (and DARTree terms)
+ * the tree step reads; its contents are meaningless between calls. */
 size_t dt_workspace_size(const dt_params* params);
 
 /* Static, human-readable name of a status code. */
