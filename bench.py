@@ -60,6 +60,9 @@ def parse():
                     help="bracket every n-th B=64 sweep launch with timing events")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sweep-chunks", type=int, default=0, help="0 = the library's automatic plan")
+    ap.add_argument("--workload", default="c4p",
+                    help="c4p (the default JSON contract) or another named configuration, timed per call "
+                         "(c1, c2, c2p, c3, c3p, c4, c4L, c4Lp, c5)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -129,6 +132,11 @@ class TimingEvents:
     def destroy(self, e: int) -> None:
         self.lib.hipEventDestroy(e)
 
+    def record(self, e: int, stream: int) -> None:
+        rc = self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
 
 def copy_probe(mib: int) -> None:
     import torch
@@ -142,6 +150,92 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}))
 
 
+def run_workload(args) -> None:
+    """Per-call latency of one named configuration: calls on one stream, each
+    bracketed by fence-free events, inputs rotated over enough distinct sets
+    to exceed the Infinity Cache where the generator allows it (small
+    configurations stay cache-resident and are latency-bound anyway)."""
+    import statistics
+    import torch
+    from draft_tree_construction_dt_amd import binding as bd, synth
+
+    cfg = synth.config(args.workload)
+    bpe = 2 if cfg.dtype == synth.DTYPE_BF16 else 4
+    per_call = cfg.B * cfg.d * cfg.V * bpe
+    sets = max(1, min(-(-(800 << 20) // per_call), 1600 // cfg.B))
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    prob = synth.make_problem(args.workload, args.seed, B=cfg.B * sets)
+    print(f"[bench] {args.workload}: generated {sets} input sets in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    logits = bd.logits_tensor(prob, dev)
+    ctx = torch.from_numpy(prob.ctx).to(dev)
+    ngram = bd.upload_ngram(prob.ngram, dev)
+    E = F = None
+    if prob.mode == bd.DT_MODE_DARTREE:
+        E = torch.from_numpy(prob.E).to(dev)
+        F = torch.from_numpy(prob.F).to(dev)
+    stream = torch.cuda.current_stream()
+    pcs, keep = [], []
+    for sidx in range(sets):
+        q = bd.Params(B=cfg.B, V=prob.V, d=prob.d, k=prob.k, W=prob.W, budget=prob.budget,
+                      dtype=bd.DT_DTYPE_BF16 if bpe == 2 else bd.DT_DTYPE_F32, mode=prob.mode,
+                      ctx=ctx[sidx * cfg.B:(sidx + 1) * cfg.B], stream=stream, E=E, F=F,
+                      R=prob.E.shape[1] if E is not None else 0)
+        q.workspace = torch.empty(max(bd.dt_workspace_size(q), 16), dtype=torch.uint8, device=dev)
+        keep.append(q)
+        pcs.append(q._c())
+    out = bd.alloc_tree_out(cfg.B, prob.budget, dev)
+    out_c, ng_c = out._c(), ngram._c()
+    ptrs = [logits[sidx * cfg.B].data_ptr() for sidx in range(sets)]
+    fn = bd._load().dt_build_tree
+    tev = TimingEvents()
+    for i in range(args.warmup):
+        fn(ptrs[i % sets], ctypes.byref(ng_c), ctypes.byref(pcs[i % sets]), ctypes.byref(out_c))
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(tev.create(), tev.create()) for _ in range(K)]
+    h = stream.cuda_stream
+    t1 = time.perf_counter()
+    for i in range(K):
+        tev.record(ev[i][0], h)
+        st = fn(ptrs[i % sets], ctypes.byref(ng_c), ctypes.byref(pcs[i % sets]), ctypes.byref(out_c))
+        tev.record(ev[i][1], h)
+        if st != 0:
+            raise bd.DtError(st, "dt_build_tree")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    us = sorted(tev.elapsed_ms(a, b) * 1e3 for a, b in ev)
+    for a, b in ev:
+        tev.destroy(a)
+        tev.destroy(b)
+    med = statistics.median(us)
+    res = {
+        "metric": METRIC, "workload": args.workload, "value": cfg.B / med * 1e6, "unit": "trees/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "B": cfg.B,
+        "us_per_call_median": med, "us_per_call_p10": us[len(us) // 10], "us_per_call_p90": us[(9 * len(us)) // 10],
+        "us_per_tree": med / cfg.B, "wall_us_per_call": wall / K * 1e6,
+        "logit_bytes_per_call": per_call, "gb_per_s": per_call / med / 1e3,
+        "frac_of_8tbs": per_call / med / 1e3 / HBM_PEAK_GBS,
+        "input_sets": sets, "input_bytes_rotated": per_call * sets,
+        "cache_resident": per_call * sets < (256 << 20),
+        "data": "synthetic", "dtype": "f32",
+    }
+    if not args.no_cpu:
+        import oracle
+        n = min(prob.B, 16 if prob.mode == synth.MODE_DARTREE else 64)
+        sample = copy.copy(prob)
+        sample.B = n
+        sample.logits = prob.logits[:n]
+        sample.ctx = prob.ctx[:n]
+        tc = time.perf_counter()
+        oracle.build_tree(sample)
+        cpu_s = time.perf_counter() - tc
+        res["cpu_baseline"] = {"value": n / cpu_s, "unit": "trees/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the first {n} requests, single-threaded C, {cpu_s:.2f}s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -150,6 +244,9 @@ def main():
         sys.exit(2)
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.workload != "c4p":
+        run_workload(args)
         return
 
     import torch

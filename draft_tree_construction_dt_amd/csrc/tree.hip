@@ -56,36 +56,11 @@ extern "C" __device__ unsigned long long __ockl_wfred_max_u64(unsigned long long
 extern "C" __device__ unsigned long long __ockl_wfred_min_u64(unsigned long long);
 extern "C" __device__ int __ockl_wfred_add_i32(int);
 
-__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
-    const int lo = __builtin_amdgcn_readlane((int)(v & 0xFFFFFFFFull), l);
-    const int hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
-    return ((unsigned long long)(unsigned int)hi << 32) | (unsigned int)lo;
-}
-
 __device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
     // SplitMix64 output function (Steele, Lea, Flood).
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
     return z ^ (z >> 31);
-}
-
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
-}
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const unsigned long long o = __shfl_xor(v, off);
-        v = o > v ? o : v;
-    }
-    return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -190,135 +165,6 @@ __device__ void merge_row(const float* __restrict__ part_m, const double* __rest
 // ---------------------------------------------------------------------------
 // continuity
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool logp_keeps(const NGramArgs& a, const float* lp, int64_t e) {
-    return a.min_logp == -INFINITY || lp == nullptr || lp[e] > a.min_logp;
-}
-
-// Slot of a trigram key, or -1.  Linear probing from splitmix64(key): the
-// aligned group of 8 slots holding the probe position is read with four
-// 16-byte loads, so a chain costs one memory round trip per 8 slots.
-typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ long long find_slot(const NGramArgs& a, unsigned long long key) {
-    const unsigned long long cm = (unsigned long long)a.cap - 1ull;
-    unsigned long long pos = mix64(key) & cm;
-    if (a.cap < 8) {
-        for (long long probe = 0; probe < a.cap; ++probe) {
-            const unsigned long long here = a.keys[pos];
-            if (here == key) return (long long)pos;
-            if (here == kEmptyKey) return -1;
-            pos = (pos + 1ull) & cm;
-        }
-        return -1;
-    }
-    for (long long seen = 0; seen < a.cap; seen += 8) {
-        const unsigned long long base = pos & ~7ull;
-        const u64x2* g = reinterpret_cast<const u64x2*>(a.keys + base);
-        const u64x2 q0 = g[0], q1 = g[1], q2 = g[2], q3 = g[3];
-        const unsigned long long kk[8] = {q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
-        const int start = (int)(pos - base);
-        int hit = -1;
-        bool stop = false;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            if (!stop && s >= start) {
-                if (kk[s] == key) {
-                    hit = s;
-                    stop = true;
-                } else if (kk[s] == kEmptyKey) {
-                    stop = true;
-                }
-            }
-        }
-        if (hit >= 0) return (long long)(base + hit);
-        if (stop) return -1;
-        pos = (base + 8ull) & cm;
-    }
-    return -1;
-}
-
-// Up to 16 successor ids of a row (-1 beyond n): four 16-byte loads when the
-// row is 16-byte aligned and holds whole vectors, scalar loads otherwise.
-__device__ __forceinline__ void load_row16(int (&r)[16], const int* p, int n) {
-    typedef int i4 __attribute__((ext_vector_type(4)));
-    if (n >= 16 && ((uintptr_t)p & 15u) == 0) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const i4 x = reinterpret_cast<const i4*>(p)[v];
-            r[4 * v] = x.x; r[4 * v + 1] = x.y; r[4 * v + 2] = x.z; r[4 * v + 3] = x.w;
-        }
-    } else {
-#pragma unroll
-        for (int u = 0; u < 16; ++u) r[u] = u < n ? p[u] : -1;
-    }
-}
-
-// Bit j set iff child T_{t-1}[j] (finite logit) is admitted after (a2, a1).
-__device__ uint32_t admitted_children(const NGramArgs& a, int a2, int a1, const int* ch, const float* cx, int k) {
-    uint32_t live = 0;
-    for (int j = 0; j < k; ++j)
-        if (cx[j] != -INFINITY) live |= 1u << j;
-    if (live == 0) return 0;
-    // context ids come from the caller's ctx for the first depths: ids outside
-    // [0, V) index no table row and admit nothing
-    const bool bigram = a.kind == DT_NGRAM_DENSE_BIGRAM || a.kind == DT_NGRAM_CSR_BIGRAM;
-    if (bigram && (a1 < 0 || a1 >= a.V)) return 0;
-    uint32_t m = 0;
-    if (a.kind == DT_NGRAM_DENSE_BIGRAM) {
-        const float* row = a.dense + (int64_t)a1 * a.V;
-        for (int j = 0; j < k; ++j)
-            if (row[ch[j]] > a.min_logp) m |= 1u << j;
-    } else if (a.kind == DT_NGRAM_CSR_BIGRAM) {
-        const int lo = a.row_ptr[a1], hi = a.row_ptr[a1 + 1];
-        if (hi - lo <= 64) {
-            for (int e = lo; e < hi; ++e) {
-                const int c = a.col[e];
-                for (int j = 0; j < k; ++j)
-                    if (ch[j] == c && logp_keeps(a, a.csr_logp, e)) m |= 1u << j;
-            }
-        } else {
-            for (int j = 0; j < k; ++j) {       // rows are ascending: binary search
-                int l = lo, h = hi;
-                while (l < h) {
-                    const int mid = (l + h) >> 1;
-                    if (a.col[mid] < ch[j]) l = mid + 1; else h = mid;
-                }
-                if (l < hi && a.col[l] == ch[j] && logp_keeps(a, a.csr_logp, l)) m |= 1u << j;
-            }
-        }
-    } else if (a.kind == DT_NGRAM_HASH_TRIGRAM) {
-        const unsigned long long key = ((unsigned long long)(uint32_t)a2 << 32) | (uint32_t)a1;
-        // the successor row of the home slot is read while the key group is
-        // probed: a present key usually sits in its home slot
-        const long long home = (long long)(mix64(key) & ((unsigned long long)a.cap - 1ull));
-        int spec[16];
-        load_row16(spec, a.succ + home * a.S, a.S);
-        const long long slot = find_slot(a, key);
-        if (slot < 0) return 0;
-        const int* succ = a.succ + slot * a.S;
-        const bool membership = a.min_logp == -INFINITY || a.hash_logp == nullptr;
-        for (int s0 = 0; s0 < a.S; s0 += 16) {
-            int reg[16];
-            if (slot == home && s0 == 0) {
-#pragma unroll
-                for (int u = 0; u < 16; ++u) reg[u] = spec[u];
-            } else {
-                load_row16(reg, succ + s0, a.S - s0);
-            }
-            for (int j = 0; j < k; ++j) {
-                const int c = ch[j];
-                int hs = -1;
-#pragma unroll
-                for (int u = 0; u < 16; ++u) hs = reg[u] == c ? s0 + u : hs;
-                if (hs >= 0 && (membership || a.hash_logp[slot * a.S + hs] > a.min_logp)) m |= 1u << j;
-            }
-        }
-    } else {
-        m = live;
-    }
-    return m & live;
-}
-
 // Children of one depth by token: an open-addressing table in LDS
 // (kChildSlots slots, load <= 1/4) maps a token to its index in T_{t-1}.
 constexpr int kChildSlots = 128;
@@ -416,6 +262,51 @@ __device__ uint32_t quad_admitted(const NGramArgs& a, int a2, int a1, bool activ
     return quad_or(hit) & live;
 }
 
+// Admissible children after the bigram context a1, by the four lanes of a
+// quad (g = lane & 3): a dense row is read at the children's columns (lane g
+// takes children g, g+4, ...); a CSR row is read 64 successors per round
+// trip (lane g takes 4g..4g+3 of every 16), each mapped to its child index
+// through the LDS token table.  Inactive quads and ids outside [0, V) admit
+// nothing.  The result is the same in all four lanes.
+__device__ uint32_t quad_admitted_bigram(const NGramArgs& a, int a1, bool active, int g, const int* ch,
+                                         const int* ctok, const int* cj, uint32_t live, int k) {
+    if (!active || a1 < 0 || a1 >= a.V) return 0u;               // the same in the whole quad
+    uint32_t hit = 0;
+    if (a.kind == DT_NGRAM_DENSE_BIGRAM) {
+        const float* row = a.dense + (int64_t)a1 * a.V;
+        float v[kMaxK / 4];
+#pragma unroll
+        for (int u = 0; u < kMaxK / 4; ++u) {
+            const int j = g + 4 * u;
+            v[u] = j < k ? row[ch[j]] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < kMaxK / 4; ++u) {
+            const int j = g + 4 * u;
+            if (j < k && v[u] > a.min_logp) hit |= 1u << j;
+        }
+    } else {
+        const int lo = a.row_ptr[a1], hi = a.row_ptr[a1 + 1];
+        const bool membership = a.min_logp == -INFINITY || a.csr_logp == nullptr;
+        for (int e0 = lo; e0 < hi; e0 += 64) {
+            int sv[16];
+            float lp[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int e = e0 + 16 * (u >> 2) + 4 * g + (u & 3);
+                sv[u] = e < hi ? a.col[e] : -1;
+                lp[u] = (!membership && e < hi) ? a.csr_logp[e] : INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int j = child_index(ctok, cj, sv[u]);
+                if (j >= 0 && (membership || lp[u] > a.min_logp)) hit |= 1u << j;
+            }
+        }
+    }
+    return quad_or(hit) & live;
+}
+
 // Index of a continuity context.  Depth t's contexts: bigram -> parent token
 // (t = 1: the root; t >= 2: T_{t-2}[i1]); trigram -> (grandparent, parent)
 // (t = 1: (ctx0, ctx1); t = 2: (ctx1, T_0[i1]); t >= 3: (T_{t-3}[i2], T_{t-2}[i1])).
@@ -431,10 +322,6 @@ __device__ __forceinline__ int ctx_index(int kind, int k, int t, int i2, int i1)
 // ---------------------------------------------------------------------------
 // ordering keys
 // ---------------------------------------------------------------------------
-// frontier: (Rk desc, token asc, parent rank asc); tie = token << 6 | rank
-__device__ __forceinline__ bool cand_before(double rk_a, uint32_t tie_a, double rk_b, uint32_t tie_b) {
-    return rk_a > rk_b || (rk_a == rk_b && tie_a < tie_b);
-}
 // budget: (S desc, depth asc, BFS index asc); BFS index order implies depth order
 __device__ __forceinline__ bool node_before(double s_a, int i_a, double s_b, int i_b) {
     return s_a > s_b || (s_a == s_b && i_a < i_b);
@@ -548,8 +435,9 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
         }
         const int per = (n_t + a.nsplit - 1) / a.nsplit;
         const int lo = split * per, hi = lo + per < n_t ? lo + per : n_t;
-        if (trigram) {
-            // children of depth t by token, then one quad per context
+        // children of depth t by token (the trigram and CSR rows list
+        // successors by token), then one lane quad per context
+        if (kind != DT_NGRAM_DENSE_BIGRAM) {
             for (int i = tid; i < kChildSlots; i += kThreads) s_ctok[i] = -1;
             __syncthreads();
             if (tid < k) {
@@ -564,12 +452,15 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
                 }
             }
             __syncthreads();
-            uint32_t live = 0;
-            for (int j = 0; j < k; ++j) live |= (uint32_t)(s_x[0][j] != -INFINITY) << j;
-            const int g = tid & 3;
-            for (int c0 = lo; c0 < hi; c0 += kThreads / 4) {
-                const int c = c0 + (tid >> 2);
-                const bool active = c < hi;
+        }
+        uint32_t live = 0;
+        for (int j = 0; j < k; ++j) live |= (uint32_t)(s_x[0][j] != -INFINITY) << j;
+        const int g = tid & 3;
+        for (int c0 = lo; c0 < hi; c0 += kThreads / 4) {
+            const int c = c0 + (tid >> 2);
+            const bool active = c < hi;
+            uint32_t m;
+            if (trigram) {
                 int a2 = 0, a1 = 0;
                 if (active) {
                     if (t == 1) {
@@ -580,14 +471,12 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
                         a1 = t == 2 ? s_tok[1][c] : s_tok[1][c % k];
                     }
                 }
-                const uint32_t m = quad_admitted(a.ng, a2, a1, active, g, s_ctok, s_cj, live);
-                if (active && g == 0) a.vmask[(int64_t)b * a.n_ctx + base + c] = m;
+                m = quad_admitted(a.ng, a2, a1, active, g, s_ctok, s_cj, live);
+            } else {
+                const int a1 = !active ? 0 : (t == 1 ? ctx1 : s_tok[1][c]);
+                m = quad_admitted_bigram(a.ng, a1, active, g, s_tok[0], s_ctok, s_cj, live, k);
             }
-        } else {
-            for (int c = lo + tid; c < hi; c += kThreads) {
-                const int a1 = t == 1 ? ctx1 : s_tok[1][c];
-                a.vmask[(int64_t)b * a.n_ctx + base + c] = admitted_children(a.ng, 0, a1, s_tok[0], s_x[0], k);
-            }
+            if (active && g == 0) a.vmask[(int64_t)b * a.n_ctx + base + c] = m;
         }
     }
 
