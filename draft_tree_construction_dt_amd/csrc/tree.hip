@@ -756,7 +756,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
         if (lane == 0) misc[0] = nb;
     }
     __syncthreads();
-    nb = *(volatile int*)&misc[0];
+    nb = misc[0];                                            // ordered by the barrier
 
     // ---- 5. verification budget
     int n_sel = nb;
@@ -873,16 +873,47 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
         }
     }
     const int words = a.mask_words;
-    for (int e = tid; e < budget * words; e += kTreeThreads) {
-        const int o = e / words, w = e - o * words;
-        uint32_t bits = 0;
-        if (o < n_sel) {
-            for (int i = n_out[o]; i >= 0; i = n_par[i]) {
-                const int ni = n_new[i];
-                if ((ni >> 5) == w) bits |= 1u << (ni & 31);
+    if (budget * words > kTreeThreads && words <= 8) {
+        // more (node, word) pairs than threads: one thread per node walks its
+        // ancestors once and sets their bits in all its words
+        for (int o = tid; o < budget; o += kTreeThreads) {
+            uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0, a4 = 0, a5 = 0, a6 = 0, a7 = 0;
+            if (o < n_sel) {
+                for (int i = n_out[o]; i >= 0; i = n_par[i]) {
+                    const int ni = n_new[i];
+                    const uint32_t bit = 1u << (ni & 31), wd = (uint32_t)ni >> 5;
+                    a0 |= wd == 0 ? bit : 0u;
+                    a1 |= wd == 1 ? bit : 0u;
+                    a2 |= wd == 2 ? bit : 0u;
+                    a3 |= wd == 3 ? bit : 0u;
+                    a4 |= wd == 4 ? bit : 0u;
+                    a5 |= wd == 5 ? bit : 0u;
+                    a6 |= wd == 6 ? bit : 0u;
+                    a7 |= wd == 7 ? bit : 0u;
+                }
             }
+            uint32_t* row = a.mask + (ob + o) * words;
+            row[0] = a0;
+            if (words > 1) row[1] = a1;
+            if (words > 2) row[2] = a2;
+            if (words > 3) row[3] = a3;
+            if (words > 4) row[4] = a4;
+            if (words > 5) row[5] = a5;
+            if (words > 6) row[6] = a6;
+            if (words > 7) row[7] = a7;
         }
-        a.mask[ob * words + e] = bits;
+    } else {
+        for (int e = tid; e < budget * words; e += kTreeThreads) {
+            const int o = e / words, w = e - o * words;
+            uint32_t bits = 0;
+            if (o < n_sel) {
+                for (int i = n_out[o]; i >= 0; i = n_par[i]) {
+                    const int ni = n_new[i];
+                    if ((ni >> 5) == w) bits |= 1u << (ni & 31);
+                }
+            }
+            a.mask[ob * words + e] = bits;
+        }
     }
     if (tid == 0) a.n_nodes[b] = n_sel;
 }
