@@ -77,7 +77,7 @@ TreePlan plan_tree(const dt_params* p, int kind) {
         return o;
     };
     P.off_lse = take(d * 8, 8);
-    P.off_g = take(p->mode == DT_MODE_DARTREE ? d * k * k * 8 : 0, 8);
+    P.off_g = take(p->mode == DT_MODE_DARTREE ? d * k * k * 8 : 0, 16);
     P.off_ttok = take(d * k * 4, 4);
     P.off_tx = take(d * k * 4, 4);
     P.off_vmask = take(P.n_ctx * 4, 4);

@@ -567,8 +567,31 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
             s_tx[i] = a.tx[r0 * k + i];
         }
         for (int i = tid; i < P.n_ctx; i += kTreeThreads) s_vmask[i] = a.vmask[(int64_t)b * a.n_ctx + i];
-        if (dartree)
-            for (int i = tid; i < d * k * k; i += kTreeThreads) s_g[i] = a.g[r0 * k * k + i];
+        if (dartree) {
+            const double* gsrc = a.g + r0 * k * k;
+            const int ng = d * k * k;
+            if ((((uintptr_t)gsrc | (uintptr_t)s_g) & 15u) == 0 && (ng & 1) == 0) {
+                // 16-byte vectors, four in flight per thread before the stores
+                typedef double d2 __attribute__((ext_vector_type(2)));
+                const d2* src = reinterpret_cast<const d2*>(gsrc);
+                d2* dst = reinterpret_cast<d2*>(s_g);
+                const int nv = ng >> 1;
+                for (int base = 0; base < nv; base += 4 * kTreeThreads) {
+                    d2 v0, v1, v2, v3;
+                    const int i0 = base + tid, i1 = i0 + kTreeThreads, i2 = i1 + kTreeThreads, i3 = i2 + kTreeThreads;
+                    if (i0 < nv) v0 = src[i0];
+                    if (i1 < nv) v1 = src[i1];
+                    if (i2 < nv) v2 = src[i2];
+                    if (i3 < nv) v3 = src[i3];
+                    if (i0 < nv) dst[i0] = v0;
+                    if (i1 < nv) dst[i1] = v1;
+                    if (i2 < nv) dst[i2] = v2;
+                    if (i3 < nv) dst[i3] = v3;
+                }
+            } else {
+                for (int i = tid; i < ng; i += kTreeThreads) s_g[i] = gsrc[i];
+            }
+        }
     }
     __syncthreads();
 
