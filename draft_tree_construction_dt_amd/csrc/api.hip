@@ -15,22 +15,31 @@ SweepPlan plan_sweep(const dt_params* p) {
     s.rows = (int64_t)p->B * p->d;
     const int V = p->V;
     int C;
+    int lists = kWaves;
+    const int64_t by_merge4 = kMergeKeysPerRow / (p->k * kWaves);     // chunks with one list per wave
+    const int64_t by_merge1 = kMergeKeysPerRow / p->k;                // chunks with one list per chunk
     if (p->sweep_chunks > 0) {
         C = p->sweep_chunks;
+        if (C > by_merge4) lists = 1;
     } else {
-        // at least ~two 256-thread workgroups per CU (256 CUs), chunks of
-        // >= 4096 elements, and a cross-chunk merge of <= kMergeKeysPerRow keys
+        // at least ~two 256-thread workgroups per CU (256 CUs) and chunks of
+        // >= 4096 elements; a row merges at most kMergeKeysPerRow keys, so
+        // short chunks (small batches) merge their four wave lists in the
+        // workgroup first
         const int64_t target = 512;
         int64_t c = s.rows >= target ? 1 : ceil_div(target, s.rows > 0 ? s.rows : 1);
         const int64_t by_len = V / 4096 > 1 ? V / 4096 : 1;
-        const int64_t by_merge = kMergeKeysPerRow / (p->k * kWaves);
         if (c > by_len) c = by_len;
-        if (c > by_merge) c = by_merge;
+        if (c > by_merge4) {
+            lists = 1;
+            if (c > by_merge1) c = by_merge1;
+        }
         C = (int)(c < 1 ? 1 : c);
     }
     if (C > V) C = V;
     s.chunk = (int)round_up(ceil_div(V, C), 8);
     s.C = (int)ceil_div(V, s.chunk);
+    s.lists = lists;
     return s;
 }
 
@@ -42,7 +51,7 @@ int n_contexts(int kind, int d, int k) {
 
 WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s) {
     WorkspacePlan w{};
-    const int64_t n = s.rows * s.C * kWaves;     // one partial list per sweep wave
+    const int64_t n = s.rows * s.C * s.lists;    // partial lists
     const int64_t rows = s.rows, k = p->k;
     w.n_ctx_cap = n_contexts(DT_NGRAM_HASH_TRIGRAM, p->d, p->k);   // the largest kind
     int64_t off = 0;
@@ -111,7 +120,7 @@ static dt_status check_shape(const dt_params* p) {
         p->W * p->k > kMaxCandidates || p->V >= kMaxV)
         return DT_ERR_UNSUPPORTED;
     const SweepPlan s = plan_sweep(p);
-    if ((int64_t)s.C * kWaves * p->k > kMergeKeysPerRow) return DT_ERR_UNSUPPORTED;
+    if ((int64_t)s.C * s.lists * p->k > kMergeKeysPerRow || (int64_t)s.C * s.lists > 256) return DT_ERR_UNSUPPORTED;
     return DT_OK;
 }
 
@@ -175,6 +184,7 @@ static dt_status launch_sweep_for(const void* logits, const dt_params* p, const 
     sa.V = p->V;
     sa.C = s.C;
     sa.chunk = s.chunk;
+    sa.lists = s.lists;
     sa.k = p->k;
     sa.part_m = (float*)(ws + w.off_m);
     sa.part_s = (double*)(ws + w.off_s);
@@ -215,7 +225,7 @@ extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngr
     pa.B = p->B;
     pa.d = p->d;
     pa.k = p->k;
-    pa.L = s.C * kWaves;                          // partial lists per row
+    pa.L = s.C * s.lists;                         // partial lists per row
     pa.mode = p->mode;
     pa.R = p->R;
     pa.n_ctx = w.n_ctx_cap;
@@ -286,7 +296,7 @@ extern "C" dt_status dt_position_topk(const void* logits, const dt_params* p, do
     char* ws = (char*)p->workspace;
     MergeArgs ma{};
     ma.rows = (int)s.rows;
-    ma.C = s.C * kWaves;
+    ma.C = s.C * s.lists;
     ma.k = p->k;
     ma.part_m = (const float*)(ws + w.off_m);
     ma.part_s = (const double*)(ws + w.off_s);

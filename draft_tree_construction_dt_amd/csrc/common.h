@@ -50,14 +50,15 @@ __host__ __device__ inline uint32_t unord_bits(uint32_t o) {
 struct SweepPlan {
     int C;
     int chunk;
+    int lists;          // partial lists per chunk: kWaves (one per wave) or 1 (merged in the workgroup)
     int64_t rows;
 };
 
-// Workspace: per (row, chunk, sweep wave) partial results of the sweep, then
+// Workspace: per (row, chunk[, sweep wave]) partial results of the sweep, then
 // what the prep kernel derives from them for the tree kernel.
-//   part_m    float  [rows][C*4]      running max of the wave's elements
-//   part_s    double [rows][C*4]      sum exp(x - part_m) over them
-//   part_keys uint64 [rows][C*4][k]   their top-k keys, descending; 0 pads
+//   part_m    float  [rows][C*L]      running max of the list's elements (L = lists per chunk)
+//   part_s    double [rows][C*L]      sum exp(x - part_m) over them
+//   part_keys uint64 [rows][C*L][k]   their top-k keys, descending; 0 pads
 //   lse       double [rows]           log-softmax normaliser of each row
 //   ttok      int32  [rows][k]        top-k token ids (T_i), value desc, id asc
 //   tx        float  [rows][k]        their logits
@@ -91,6 +92,7 @@ struct SweepArgs {
     int V;
     int C;
     int chunk;
+    int lists;
     int k;
     float* part_m;
     double* part_s;

@@ -307,18 +307,68 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
         }
     }
 
-    // ---- this wave's partial: its top-k sorted, and (max, sum exp(x - max));
-    //      every wave writes its own list, so waves never wait for each other
+    // ---- this wave's partial: its top-k sorted, and (max, sum exp(x - max))
     wave_select(buf, st, k, lane);
     const float M = __ockl_wfred_max_f32(st.m);
     const double sl = (st.m == -INFINITY) ? 0.0 : st.s * (double)__builtin_amdgcn_exp2f((st.m - M) * kLog2e);
     const double S = __ockl_wfred_add_f64(sl);
-    const int64_t list = (row * a.C + chunk) * kWaves + wave;
-    unsigned long long* out = a.part_keys + list * k;
-    if (lane < k) out[lane] = lane < st.cnt ? buf[lane] : 0ull;
+    if (a.lists == kWaves) {
+        // every wave writes its own list, so waves never wait for each other
+        const int64_t list = (row * a.C + chunk) * kWaves + wave;
+        unsigned long long* out = a.part_keys + list * k;
+        if (lane < k) out[lane] = lane < st.cnt ? buf[lane] : 0ull;
+        if (lane == 0) {
+            a.part_m[list] = M;
+            a.part_s[list] = S;
+        }
+        return;
+    }
+    // one list per workgroup (small batches use many short chunks, so the
+    // rows' merges stay small): wave 0 merges the four wave partials
+    __shared__ unsigned long long s_all[kWaves * kMaxK + 8];
+    __shared__ float s_wm[kWaves];
+    __shared__ double s_ws[kWaves];
+    if (lane < k) s_all[wave * k + lane] = lane < st.cnt ? buf[lane] : 0ull;
     if (lane == 0) {
-        a.part_m[list] = M;
-        a.part_s[list] = S;
+        s_wm[wave] = M;
+        s_ws[wave] = S;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const int n = kWaves * k, n8 = (n + 7) & ~7;
+    if (lane < n8 - n) s_all[n + lane] = 0ull;          // pad: 0 beats nothing
+    const float mw = lane < kWaves ? s_wm[lane] : -INFINITY;
+    const float Mall = __ockl_wfred_max_f32(mw);
+    const double sw = (lane < kWaves && mw != -INFINITY)
+                          ? s_ws[lane] * (double)__builtin_amdgcn_exp2f((mw - Mall) * kLog2e) : 0.0;
+    const double Sall = __ockl_wfred_add_f64(sw);
+    const unsigned long long ka = lane < n ? s_all[lane] : 0ull;
+    const unsigned long long kb = lane + 64 < n ? s_all[lane + 64] : 0ull;
+    int ra = 0, rb = 0;
+    for (int j = 0; j < n8; j += 8) {
+        unsigned long long v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = s_all[j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            ra += v[u] > ka;
+            rb += v[u] > kb;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ranks of the nonzero keys are 0..(count-1) (keys are unique); slots
+    // past the count keep the zero written first
+    unsigned long long* sel = buf;                       // wave 0's buffer is free now
+    if (lane < k) sel[lane] = 0ull;
+    __builtin_amdgcn_wave_barrier();
+    if (ka != 0ull && ra < k) sel[ra] = ka;
+    if (kb != 0ull && rb < k) sel[rb] = kb;
+    __builtin_amdgcn_wave_barrier();
+    const int64_t list = row * a.C + chunk;
+    if (lane < k) a.part_keys[list * k + lane] = sel[lane];
+    if (lane == 0) {
+        a.part_m[list] = Mall;
+        a.part_s[list] = Sall;
     }
 }
 
