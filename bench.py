@@ -59,6 +59,7 @@ def parse():
     ap.add_argument("--event-every", type=int, default=8,
                     help="bracket every n-th B=64 sweep launch with timing events")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--update-steps", type=int, default=2000, help="timed trigram-table update calls")
     ap.add_argument("--sweep-chunks", type=int, default=0, help="0 = the library's automatic plan")
     ap.add_argument("--workload", default="c4p",
                     help="c4p (the default JSON contract) or another named configuration, timed per call "
@@ -236,6 +237,60 @@ def run_workload(args) -> None:
     print(json.dumps(res), flush=True)
 
 
+def time_ngram_update(lib, ngram, prob, dev, K: int, warmup: int, seed: int) -> dict:
+    """Back-to-back dt_ngram_update calls on one stream, each adding the
+    accepted tokens of B=64 requests (d+1 each: the d drafted positions and the
+    bonus token) to a copy of the trigram table.  Every call gets a batch of
+    its own with uniform ids, so nearly every trigram is a new key: the
+    insertion path, not the lookup of trigrams already present."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from draft_tree_construction_dt_amd import binding as bd
+    tab = dataclasses.replace(ngram, keys=ngram.keys.clone(), succ=ngram.succ.clone(),
+                              hash_logp=None if ngram.hash_logp is None else ngram.hash_logp.clone())
+    g = tab._c()
+    L = prob.d + 1
+    n = warmup + K
+    rng = np.random.default_rng(seed + 991)
+    tokens = torch.from_numpy(rng.integers(0, prob.V, size=(n, BATCH, L), dtype=np.int32)).to(dev)
+    ctx = torch.from_numpy(rng.integers(0, prob.V, size=(n, BATCH, 2), dtype=np.int32)).to(dev)
+    lengths = torch.full((BATCH,), L, dtype=torch.int32, device=dev)
+    counts = torch.zeros(3, dtype=torch.int32, device=dev)
+    h = torch.cuda.current_stream().cuda_stream
+    occupied0 = int((tab.keys != -1).sum())
+    fn = lib.dt_ngram_update
+
+    def call(i):
+        st = fn(ctypes.byref(g), ctypes.c_void_p(ctx[i].data_ptr()), ctypes.c_void_p(tokens[i].data_ptr()),
+                ctypes.c_void_p(lengths.data_ptr()), BATCH, L, 0.0, ctypes.c_void_p(counts.data_ptr()), h)
+        if st != 0:
+            raise bd.DtError(st, "dt_ngram_update")
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    c0 = counts.cpu().tolist()
+    t0 = time.perf_counter()
+    for i in range(warmup, n):
+        call(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    c1 = counts.cpu().tolist()
+    tri = K * BATCH * L
+    return {
+        "workload": f"B={BATCH} requests x {L} accepted tokens per call (uniform ids) into a copy of the "
+                    f"trigram table ({tab.cap} slots x {tab.S}, {occupied0} keys before)",
+        "us_per_call": wall / K * 1e6,
+        "trigrams_per_s": tri / wall,
+        "steps": K,
+        "keys_added": c1[0] - c0[0],
+        "successors_added": c1[1] - c0[1],
+        "dropped": c1[2] - c0[2],
+        "timing": "wall clock of back-to-back calls on one stream",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -340,6 +395,8 @@ def main():
     b1_wall, _ = run(1, list(range(nreq)), K1, min(200, K1), nstream)
     b1_one, _ = run(1, list(range(nreq)), K1, min(200, K1), 1)
 
+    upd = time_ngram_update(lib, ngram, prob, dev, args.update_steps, 100, args.seed)
+
     achieved = logit_bytes / sweep_avg_s / 1e9
     traffic = stored_traffic()
     res = {
@@ -379,6 +436,7 @@ def main():
             "streams": nstream,
             "steps": K1,
         },
+        "ngram_update": upd,
         "roofline": {
             "bound": "hbm",
             "kernel": "sweep_kernel<bf16>",

@@ -67,7 +67,7 @@ class _TreeOut(ctypes.Structure):
                 ("scores", ctypes.c_void_p), ("mask", ctypes.c_void_p)]
 
 
-EXPORTED = ("dt_build_tree", "dt_workspace_size", "dt_status_string", "dt_position_topk")
+EXPORTED = ("dt_build_tree", "dt_workspace_size", "dt_status_string", "dt_position_topk", "dt_ngram_update")
 
 _lib = None
 
@@ -93,6 +93,10 @@ def _load():
         lib.dt_position_topk.restype = ctypes.c_int
         lib.dt_position_topk.argtypes = [ctypes.c_void_p, ctypes.POINTER(_Params), ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p]
+        lib.dt_ngram_update.restype = ctypes.c_int
+        lib.dt_ngram_update.argtypes = [ctypes.POINTER(_NGram), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                        ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -209,6 +213,25 @@ def dt_build_tree(logits: torch.Tensor, ngram: NGram, params: Params, out: TreeO
     st = _load().dt_build_tree(_ptr(logits), ctypes.byref(g), ctypes.byref(p), ctypes.byref(o))
     if st != DT_OK:
         raise DtError(st, "dt_build_tree")
+
+
+def dt_ngram_update(ngram: "NGram", ctx: torch.Tensor, tokens: torch.Tensor, lengths: torch.Tensor,
+                    new_logp: float = 0.0, counts: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Add the trigrams of the accepted tokens to a device trigram table in
+    place (see dt_ngram_update in dt.h).  ctx int32 [B][2], tokens int32
+    [B][L], lengths int32 [B], counts int32 [3] or None; all on the device."""
+    g = ngram._c()
+    B, L = (int(tokens.shape[0]), int(tokens.shape[1])) if tokens.dim() == 2 else (0, 0)
+    if stream is None:
+        h = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    elif isinstance(stream, int):
+        h = stream
+    else:
+        h = stream.cuda_stream
+    st = _load().dt_ngram_update(ctypes.byref(g), _ptr(ctx), _ptr(tokens), _ptr(lengths), B, L,
+                                 float(new_logp), _ptr(counts), h)
+    if st != DT_OK:
+        raise DtError(st, "dt_ngram_update")
 
 
 def dt_position_topk(logits: torch.Tensor, params: Params, lse: torch.Tensor, topk_tok: torch.Tensor,

@@ -307,3 +307,33 @@ extern "C" dt_status dt_position_topk(const void* logits, const dt_params* p, do
     if (launch_merge(ma, (hipStream_t)p->stream) != hipSuccess) return DT_ERR_HIP;
     return DT_OK;
 }
+
+extern "C" dt_status dt_ngram_update(const dt_ngram_table* table, const int32_t* ctx, const int32_t* tokens,
+                                     const int32_t* lengths, int32_t B, int32_t L, float new_logp,
+                                     int32_t* counts, void* stream) {
+    if (!table || table->kind != DT_NGRAM_HASH_TRIGRAM) return DT_ERR_INVALID_ARG;
+    if (B < 0 || L < 0 || isnan(new_logp)) return DT_ERR_INVALID_ARG;
+    if (!table->keys || !table->succ || table->cap < 2 || (table->cap & (table->cap - 1)) != 0)
+        return DT_ERR_INVALID_ARG;
+    if (((uintptr_t)table->keys & 7u) != 0 || ((uintptr_t)table->succ & 3u) != 0 ||
+        ((uintptr_t)table->hash_logp & 3u) != 0)
+        return DT_ERR_INVALID_ARG;
+    if (table->S < 1 || table->S > 64) return DT_ERR_UNSUPPORTED;
+    if ((int64_t)B * L == 0) return DT_OK;
+    if (!ctx || !tokens || !lengths) return DT_ERR_INVALID_ARG;
+    NGramUpdateArgs a{};
+    a.B = B;
+    a.L = L;
+    a.S = table->S;
+    a.cap = table->cap;
+    a.new_logp = new_logp;
+    a.ctx = ctx;
+    a.tokens = tokens;
+    a.lengths = lengths;
+    a.keys = (unsigned long long*)table->keys;           // the update writes the table in place
+    a.succ = (int32_t*)table->succ;
+    a.hash_logp = (float*)table->hash_logp;
+    a.counts = counts;
+    if (launch_ngram_update(a, (hipStream_t)stream) != hipSuccess) return DT_ERR_HIP;
+    return DT_OK;
+}

@@ -147,6 +147,19 @@ struct TreeArgs {
     TreePlan plan;
 };
 
+struct NGramUpdateArgs {
+    int B, L, S;
+    long long cap;
+    float new_logp;
+    const int32_t* ctx;
+    const int32_t* tokens;
+    const int32_t* lengths;
+    unsigned long long* keys;
+    int32_t* succ;
+    float* hash_logp;
+    int* counts;
+};
+
 struct MergeArgs {
     int rows, C, k;
     const float* part_m;
@@ -168,5 +181,6 @@ hipError_t launch_sweep(const SweepArgs& a, int64_t rows, int dtype, hipStream_t
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_ngram_update(const NGramUpdateArgs& a, hipStream_t stream);
 
 }  // namespace dt

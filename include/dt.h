@@ -190,6 +190,38 @@ const char* dt_status_string(dt_status s);
 dt_status dt_position_topk(const void* logits, const dt_params* params,
                            double* lse, int32_t* topk_tok, float* topk_val);
 
+/* The step after verification: keep a trigram table current with the tokens
+ * the target accepted (the N-gram model that keeps DART's expansions
+ * continuous, DART Fig. 3).  For request b the stream ctx[b][0], ctx[b][1],
+ * tokens[b][0 .. lengths[b]-1] contributes, for every accepted token s_i,
+ * the trigram (s_{i-2}, s_{i-1}) -> s_i:
+ *   - a missing key takes the first free slot of its probe sequence (the
+ *     layout dt_build_tree reads: first free slot at or after
+ *     splitmix64(key) & (cap - 1), linear probing); its row starts empty,
+ *     so rows of free slots must hold -1 in every entry;
+ *   - a missing successor takes the first -1 entry of the key's row and,
+ *     when table->hash_logp is not NULL, the log-probability new_logp;
+ *   - a trigram whose row is full, whose probe sequence has no free slot, or
+ *     whose key equals the free-slot marker is dropped.
+ * The trigrams of one call are applied concurrently: the resulting keys and
+ * successor sets are those of applying them one by one in any order as long
+ * as no row fills up and the table keeps free slots; the slot a new key lands
+ * in, and which successors an overflowing row keeps, may vary between runs.
+ * table: kind DT_NGRAM_HASH_TRIGRAM; its keys, succ and (if not NULL)
+ *   hash_logp arrays are written in place (keys 8-byte, succ and hash_logp
+ *   4-byte aligned).
+ * ctx: device [B][2] int32; tokens: device [B][L] int32; lengths: device [B]
+ *   int32 (entries past lengths[b], or past L, are ignored).
+ * counts: device int32[3] or NULL; atomically incremented by keys added,
+ *   successors added and trigrams dropped (the caller zeroes it).
+ * Must not run concurrently with a dt_build_tree reading the same table.
+ * Errors: DT_ERR_INVALID_ARG for a non-trigram table, null or misaligned
+ *   arrays, cap not a power of two >= 2, B or L < 0 or a NaN new_logp;
+ *   DT_ERR_UNSUPPORTED for S outside 1..64; DT_ERR_HIP if the launch fails. */
+dt_status dt_ngram_update(const dt_ngram_table* table, const int32_t* ctx, const int32_t* tokens,
+                          const int32_t* lengths, int32_t B, int32_t L, float new_logp,
+                          int32_t* counts, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

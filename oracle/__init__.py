@@ -74,6 +74,10 @@ def _load():
         lib.oracle_continuity.restype = ctypes.c_int
         lib.oracle_continuity.argtypes = [ctypes.POINTER(_NGram), ctypes.c_int64, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_int32]
+        lib.oracle_ngram_update.restype = ctypes.c_int
+        lib.oracle_ngram_update.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
         lib.oracle_build_tree.restype = ctypes.c_int
         lib.oracle_build_tree.argtypes = [
             ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
@@ -173,3 +177,29 @@ def build_tree(p, *, W=None, budget=None, ngram=None) -> dict:
     if rc != 0:
         raise ValueError("oracle_build_tree rejected its arguments")
     return out
+
+
+def ngram_update(ngram, ctx, tokens, lengths, new_logp: float = 0.0):
+    """Apply the accepted tokens to a trigram table in place (numpy arrays
+    ngram.keys, ngram.succ and, if present, ngram.hash_logp), sequentially in
+    stream order.  ctx int32[B][2], tokens int32[B][L], lengths int32[B].
+    Returns (keys added, successors added, trigrams dropped)."""
+    keys = ngram.keys
+    succ = ngram.succ
+    lp = getattr(ngram, "hash_logp", None)
+    for a, dt in ((keys, np.uint64), (succ, np.int32)):
+        if a.dtype != dt or not a.flags.c_contiguous:
+            raise ValueError("table arrays must be contiguous uint64 keys and int32 succ")
+    if lp is not None and (lp.dtype != np.float32 or not lp.flags.c_contiguous):
+        raise ValueError("hash_logp must be contiguous float32")
+    ctx = np.ascontiguousarray(ctx, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+    B, L = tokens.shape
+    counts = np.zeros(3, dtype=np.int64)
+    rc = _load().oracle_ngram_update(keys.ctypes.data, succ.ctypes.data, _ptr(lp), int(ngram.cap), int(ngram.S),
+                                     ctx.ctypes.data, tokens.ctypes.data, lengths.ctypes.data, int(B), int(L),
+                                     float(new_logp), counts.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_ngram_update: invalid arguments")
+    return tuple(int(x) for x in counts)

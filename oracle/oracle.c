@@ -293,3 +293,66 @@ int oracle_build_tree(const void* logits, int is_bf16, int B, int64_t V, int d, 
     free(new_index);
     return 0;
 }
+
+/* ---- keeping the trigram table current ---------------------------------- */
+
+int oracle_ngram_update(uint64_t* keys, int32_t* succ, float* hash_logp, int64_t cap, int32_t S,
+                        const int32_t* ctx, const int32_t* tokens, const int32_t* lengths,
+                        int B, int L, float new_logp, int64_t* counts) {
+    if (!keys || !succ || !ctx || !tokens || !lengths || !counts || cap < 2 || (cap & (cap - 1)) ||
+        S < 1 || B < 0 || L < 0)
+        return -1;
+    counts[0] = counts[1] = counts[2] = 0;
+    for (int b = 0; b < B; ++b) {
+        int32_t prev2 = ctx[2 * b], prev1 = ctx[2 * b + 1];
+        const int n = lengths[b] < L ? lengths[b] : L;
+        for (int i = 0; i < n; ++i) {
+            const int32_t c = tokens[(int64_t)b * L + i];
+            const uint64_t key = ((uint64_t)(uint32_t)prev2 << 32) | (uint32_t)prev1;
+            prev2 = prev1;
+            prev1 = c;
+            if (key == ~0ULL) {                   /* indistinguishable from a free slot */
+                ++counts[2];
+                continue;
+            }
+            /* find the key, or the first free slot of its probe sequence */
+            int64_t slot = -1;
+            uint64_t pos = splitmix64_mix(key) & (uint64_t)(cap - 1);
+            for (int64_t probe = 0; probe < cap; ++probe) {
+                if (keys[pos] == key) {
+                    slot = (int64_t)pos;
+                    break;
+                }
+                if (keys[pos] == ~0ULL) {
+                    keys[pos] = key;
+                    ++counts[0];
+                    slot = (int64_t)pos;
+                    break;
+                }
+                pos = (pos + 1) & (uint64_t)(cap - 1);
+            }
+            if (slot < 0) {                       /* no free slot on the way */
+                ++counts[2];
+                continue;
+            }
+            /* the successor: present already, or the first free entry */
+            int placed = 0;
+            for (int32_t e = 0; e < S; ++e) {
+                int32_t* here = &succ[slot * S + e];
+                if (*here == c) {
+                    placed = 1;
+                    break;
+                }
+                if (*here == -1) {
+                    *here = c;
+                    if (hash_logp) hash_logp[slot * S + e] = new_logp;
+                    ++counts[1];
+                    placed = 1;
+                    break;
+                }
+            }
+            if (!placed) ++counts[2];             /* row full */
+        }
+    }
+    return 0;
+}

@@ -87,6 +87,23 @@ int oracle_build_tree(const void* logits, int is_bf16, int B, int64_t V, int d, 
                       int32_t* n_nodes, int32_t* tokens, int32_t* parents,
                       int32_t* depths, float* scores, uint32_t* mask, int64_t* lookups);
 
+/* Keep a trigram table current after verification (the step after the
+ * path: "an N-gram model" that the DART pages pair with the drafter, kept
+ * from the tokens the target accepted).  For every request b, in order, the
+ * stream ctx[b][0], ctx[b][1], tokens[b][0 .. lengths[b]-1] contributes, for
+ * each accepted token s_i, the trigram (s_{i-2}, s_{i-1}) -> s_i, applied in
+ * stream order: a missing key takes the first free slot of its linear probe
+ * sequence (its successor row starts empty); a missing successor takes the
+ * first free (-1) entry of the key's row and, when the table has a logp
+ * array, the log-probability new_logp.  A trigram whose row is full, whose
+ * key finds no free slot, or whose key equals the free-slot marker is
+ * dropped.  The arrays are updated in place; counts[3] receives keys added,
+ * successors added and trigrams dropped.  Returns 0, or -1 on invalid
+ * arguments. */
+int oracle_ngram_update(uint64_t* keys, int32_t* succ, float* hash_logp, int64_t cap, int32_t S,
+                        const int32_t* ctx, const int32_t* tokens, const int32_t* lengths,
+                        int B, int L, float new_logp, int64_t* counts);
+
 #ifdef __cplusplus
 }
 #endif

@@ -130,3 +130,26 @@ def test_position_topk_validation():
     p.k = 5
     p.workspace_bytes = 8
     assert f(FAKE, ctypes.byref(p), FAKE, FAKE, FAKE) == bd.DT_ERR_WORKSPACE
+
+
+def test_ngram_update_validation():
+    f = bd._load().dt_ngram_update
+    hk = dict(kind=bd.DT_NGRAM_HASH_TRIGRAM, keys=FAKE, succ=FAKE, cap=1024, S=16)
+
+    def call(ng, B=2, L=3, logp=0.0, ctx=FAKE, tok=FAKE, lens=FAKE):
+        g = ng._c()
+        return f(ctypes.byref(g), ctx, tok, lens, B, L, logp, 0, 0)
+
+    assert f(None, FAKE, FAKE, FAKE, 1, 1, 0.0, 0, 0) == bd.DT_ERR_INVALID_ARG
+    assert call(bd.NGram(**dict(hk, kind=bd.DT_NGRAM_CSR_BIGRAM))) == bd.DT_ERR_INVALID_ARG
+    assert call(bd.NGram(**dict(hk, cap=1000))) == bd.DT_ERR_INVALID_ARG     # not a power of two
+    assert call(bd.NGram(**dict(hk, cap=1))) == bd.DT_ERR_INVALID_ARG
+    assert call(bd.NGram(**dict(hk, keys=FAKE + 4))) == bd.DT_ERR_INVALID_ARG  # keys not 8-byte aligned
+    assert call(bd.NGram(**dict(hk, hash_logp=FAKE + 2))) == bd.DT_ERR_INVALID_ARG
+    assert call(bd.NGram(**dict(hk, succ=0))) == bd.DT_ERR_INVALID_ARG
+    assert call(bd.NGram(**dict(hk, S=0))) == bd.DT_ERR_UNSUPPORTED
+    assert call(bd.NGram(**hk), B=-1) == bd.DT_ERR_INVALID_ARG
+    assert call(bd.NGram(**hk), logp=math.nan) == bd.DT_ERR_INVALID_ARG
+    assert call(bd.NGram(**hk), tok=0) == bd.DT_ERR_INVALID_ARG
+    assert call(bd.NGram(**hk), B=0) == bd.DT_OK                             # nothing to add: no launch
+    assert call(bd.NGram(**hk), L=0, tok=0) == bd.DT_OK
