@@ -50,7 +50,7 @@ import numpy as np
 # ---- enumerations shared by the C ABI (include/dt.h) and the oracle ----
 NGRAM_NONE, NGRAM_DENSE_BIGRAM, NGRAM_CSR_BIGRAM, NGRAM_HASH_TRIGRAM = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
-MODE_DART, MODE_DARTREE = 0, 1
+MODE_DART, MODE_DARTREE, MODE_DARTREE_FULL = 0, 1, 2
 EMPTY_KEY = np.uint64(0xFFFFFFFFFFFFFFFF)
 
 _M64 = np.uint64(0xFFFFFFFFFFFFFFFF)
@@ -189,6 +189,8 @@ _BASE = {
     "c4L": Config("c4L", B=64, V=32000, d=8, k=8, W=8, budget=60, plus8=True,
                   ngram=NGRAM_HASH_TRIGRAM, ngram_ids="uniform"),
     "c5": Config("c5", B=8, V=151936, d=16, k=16, W=16, budget=256, mode=MODE_DARTREE),
+    # c5 with every node proposing its own W tokens from the whole vocabulary
+    "c5f": Config("c5f", B=8, V=151936, d=16, k=16, W=16, budget=256, mode=MODE_DARTREE_FULL),
 }
 
 CONFIGS = dict(_BASE)
@@ -508,7 +510,7 @@ def make_problem(name: str, seed: int = 0, **overrides) -> Problem:
             _plant_hash(table, plans)
     E = F = None
     R = 0
-    if cfg.mode == MODE_DARTREE:
+    if cfg.mode != MODE_DART:
         _, _, ef_ss = _streams(cfg, seed)
         rng = np.random.default_rng(ef_ss)
         E = (rng.standard_normal((cfg.V, cfg.R), dtype=np.float32) * np.float32(cfg.ef_sigma))
@@ -568,9 +570,9 @@ def random_problem(rng: np.random.Generator, *, B: int, V: int, d: int, k: int, 
             logp[slot_of[i], :m] = rng.standard_normal(m) - 1.0
         ng.keys, ng.succ, ng.hash_logp, ng.cap, ng.S = table, succ, logp, hash_cap, S
     E = F = None
-    if mode == MODE_DARTREE:
+    if mode != MODE_DART:
         E = (rng.standard_normal((V, R)) * 0.5).astype(np.float32)
         F = (rng.standard_normal((V, R)) * 0.5).astype(np.float32)
     return Problem(name="random", seed=-1, B=B, V=V, d=d, k=k, W=W, budget=budget,
                    dtype=dtype, mode=mode, logits=logits, ctx=ctx, ngram=ng, E=E, F=F,
-                   R=R if mode == MODE_DARTREE else 0)
+                   R=R if mode != MODE_DART else 0)

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 # enumerations as oracle.h defines them (kept here, not imported, on purpose)
 NGRAM_NONE, NGRAM_DENSE_BIGRAM, NGRAM_CSR_BIGRAM, NGRAM_HASH_TRIGRAM = 0, 1, 2, 3
-MODE_DART, MODE_DARTREE = 0, 1
+MODE_DART, MODE_DARTREE, MODE_DARTREE_FULL = 0, 1, 2
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 

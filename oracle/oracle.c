@@ -160,7 +160,9 @@ int oracle_build_tree(const void* logits, int is_bf16, int B, int64_t V, int d, 
                       int32_t* n_nodes, int32_t* tokens, int32_t* parents,
                       int32_t* depths, float* scores, uint32_t* mask, int64_t* lookups) {
     if (B < 0 || V < 1 || d < 1 || k < 1 || k > V || W < 1 || budget < 1) return -1;
-    if (mode == ORACLE_MODE_DARTREE && (E == NULL || F == NULL || R < 1)) return -1;
+    if (mode != ORACLE_MODE_DART && mode != ORACLE_MODE_DARTREE && mode != ORACLE_MODE_DARTREE_FULL) return -1;
+    if (mode != ORACLE_MODE_DART && (E == NULL || F == NULL || R < 1)) return -1;
+    const int full = mode == ORACLE_MODE_DARTREE_FULL;
     const int words = (budget + 31) / 32;
     const size_t esize = is_bf16 ? 2 : 4;
 
@@ -168,7 +170,9 @@ int oracle_build_tree(const void* logits, int is_bf16, int B, int64_t V, int d, 
     int32_t* top_tok = (int32_t*)malloc((size_t)d * k * sizeof(int32_t));
     double* top_x = (double*)malloc((size_t)d * k * sizeof(double));
     node* nodes = (node*)malloc((size_t)d * W * sizeof(node));
-    cand* cands = (cand*)malloc((size_t)W * k * sizeof(cand));
+    /* full-vocabulary mode: W proposals per frontier node, chosen from all V */
+    cand* cands = (cand*)malloc((size_t)W * (full ? W : k) * sizeof(cand));
+    cand* pool = full ? (cand*)malloc((size_t)V * sizeof(cand)) : NULL;
     int* frontier = (int*)malloc((size_t)W * sizeof(int));
     int* next = (int*)malloc((size_t)W * sizeof(int));
     char* taken = (char*)malloc((size_t)d * W);
@@ -183,7 +187,7 @@ int oracle_build_tree(const void* logits, int is_bf16, int B, int64_t V, int d, 
         for (int i = 0; i < d; ++i) {
             const char* row = req + (size_t)i * V * esize;
             lse[i] = oracle_row_lse(row, is_bf16, V);
-            oracle_row_topk(row, is_bf16, V, k, top_tok + (size_t)i * k, top_x + (size_t)i * k);
+            if (!full) oracle_row_topk(row, is_bf16, V, k, top_tok + (size_t)i * k, top_x + (size_t)i * k);
         }
 
         /* 3-4. depth loop: expand every frontier node with its depth's
@@ -201,6 +205,29 @@ int oracle_build_tree(const void* logits, int is_bf16, int B, int64_t V, int d, 
                 const double prk = p < 0 ? 0.0 : nodes[p].rk;
                 const double ps = p < 0 ? 0.0 : nodes[p].s;
                 if (ng->kind != ORACLE_NGRAM_NONE) ++nlook;
+                if (full) {
+                    /* this node's own proposals: score every token of the
+                     * vocabulary under the node's path, keep its W best */
+                    const char* row = req + (size_t)pos * V * esize;
+                    int np = 0;
+                    for (int64_t v = 0; v < V; ++v) {
+                        const double x = logit_at(row, is_bf16, v);
+                        if (x == -INFINITY) continue;
+                        if (!oracle_continuity(ng, V, pprev, ptok, (int32_t)v)) continue;
+                        const double g = dot_fp64(E + (size_t)ptok * R, F + (size_t)v * R, R);
+                        cand* cd = &pool[np++];
+                        cd->rk = (prk + x) + g;
+                        cd->s = (ps + (x - lse[pos])) + g;
+                        cd->tok = (int32_t)v;
+                        cd->parent_rank = r;
+                        cd->parent = p;
+                    }
+                    qsort(pool, (size_t)np, sizeof(cand), cand_order);
+                    const int take = np < W ? np : W;
+                    memcpy(cands + nc, pool, (size_t)take * sizeof(cand));
+                    nc += take;
+                    continue;
+                }
                 for (int j = 0; j < k; ++j) {
                     const int32_t c = top_tok[(size_t)pos * k + j];
                     const double x = top_x[(size_t)pos * k + j];
@@ -287,6 +314,7 @@ int oracle_build_tree(const void* logits, int is_bf16, int B, int64_t V, int d, 
     free(top_x);
     free(nodes);
     free(cands);
+    free(pool);
     free(frontier);
     free(next);
     free(taken);

@@ -28,7 +28,14 @@
  *  - ties: top-k by (x desc, id asc); frontier by (Rk desc, token asc,
  *    parent rank asc); budget by (S desc, depth asc, BFS index asc);
  *  - children with x = -inf (probability zero) are never expanded;
- *  - the budget counts draft nodes (root excluded).
+ *  - the budget counts draft nodes (root excluded);
+ *  - full-vocabulary DARTree mode (ORACLE_MODE_DARTREE_FULL): the drafter
+ *    proposes W tokens for every frontier node (DARTree page, "Tree
+ *    Construction"; its sketch asks for width proposals per path) from that
+ *    node's own parent-conditioned distribution over the whole vocabulary,
+ *    x[v] + E[parent_tok] . F[v]; a node's proposals are its W best tokens
+ *    under the candidate order (Rk desc, token asc), and the frontier is then
+ *    the top-W of all proposals as in the other modes.  k is not used.
  *
  * All arithmetic is double precision.  Logits are read exactly (bf16 widened
  * by a 16-bit shift).  NaN logits are undefined.
@@ -49,6 +56,7 @@ extern "C" {
 
 #define ORACLE_MODE_DART 0
 #define ORACLE_MODE_DARTREE 1
+#define ORACLE_MODE_DARTREE_FULL 2
 
 typedef struct oracle_ngram {
     int32_t kind;

@@ -20,7 +20,7 @@ import math
 import numpy as np
 
 NGRAM_NONE, NGRAM_DENSE_BIGRAM, NGRAM_CSR_BIGRAM, NGRAM_HASH_TRIGRAM = 0, 1, 2, 3
-MODE_DART, MODE_DARTREE = 0, 1
+MODE_DART, MODE_DARTREE, MODE_DARTREE_FULL = 0, 1, 2
 
 
 def logits_f64(p) -> np.ndarray:
@@ -117,7 +117,9 @@ def check_invariants(p, tree: dict, *, W=None, budget=None, score_tol=1e-4, lse=
             L = [lse_np(X[b, i]) for i in range(p.d)]
         else:
             L = lse[b]
-        if topk is None:
+        if p.mode == MODE_DARTREE_FULL:
+            T = None                       # children come from the whole vocabulary
+        elif topk is None:
             T = [set(topk_np(X[b, i], p.k).tolist()) for i in range(p.d)]
         else:
             T = [set(topk[b][i]) for i in range(p.d)]
@@ -145,7 +147,7 @@ def check_invariants(p, tree: dict, *, W=None, budget=None, score_tol=1e-4, lse=
             if i > 0 and int(dep[i]) < int(dep[i - 1]):
                 errs.append(f"b{b} n{i}: not in BFS order")
             c = int(tok[i])
-            if c not in T[t - 1]:
+            if p.mode != MODE_DARTREE_FULL and c not in T[t - 1]:
                 errs.append(f"b{b} n{i}: token {c} not in position {t - 1}'s top-k")
             x = X[b, t - 1, c]
             if x == -math.inf:
@@ -159,7 +161,7 @@ def check_invariants(p, tree: dict, *, W=None, budget=None, score_tol=1e-4, lse=
             seen.add((pi, c))
             per_depth[t] = per_depth.get(t, 0) + 1
             g = 0.0
-            if p.mode == MODE_DARTREE:
+            if p.mode != MODE_DART:
                 g = float(np.dot(p.E[ptok].astype(np.float64), p.F[c].astype(np.float64)))
             S[i] = (S[pi] if pi >= 0 else 0.0) + (x - L[t - 1]) + g
             if abs(float(sc[i]) - S[i]) > score_tol:
@@ -189,7 +191,8 @@ def all_valid_paths(p, b: int):
     X = logits_f64(p)
     cont = Continuity(p.ngram, p.V)
     L = [lse_np(X[b, i]) for i in range(p.d)]
-    T = [set(topk_np(X[b, i], p.k).tolist()) for i in range(p.d)]
+    full = p.mode == MODE_DARTREE_FULL
+    T = None if full else [set(topk_np(X[b, i], p.k).tolist()) for i in range(p.d)]
     out = {}
     frontier = {(): (0.0, 0.0)}
     ctx2, ctx1 = int(p.ctx[b, 0]), int(p.ctx[b, 1])
@@ -200,10 +203,10 @@ def all_valid_paths(p, b: int):
             pprev = (path[-2] if len(path) >= 2 else ctx1) if path else ctx2
             for c in range(p.V):
                 x = X[b, t - 1, c]
-                if c not in T[t - 1] or x == -math.inf or not cont(pprev, ptok, c):
+                if (not full and c not in T[t - 1]) or x == -math.inf or not cont(pprev, ptok, c):
                     continue
                 g = 0.0
-                if p.mode == MODE_DARTREE:
+                if p.mode != MODE_DART:
                     g = float(np.dot(p.E[ptok].astype(np.float64), p.F[c].astype(np.float64)))
                 nxt[path + (c,)] = ((s + (x - L[t - 1])) + g, (rk + x) + g)
         out.update(nxt)
@@ -222,17 +225,27 @@ def sketch_build(p, b: int, W: int):
     ctx1 = int(p.ctx[b, 1])
     nodes = {0: [()]}
     score = {(): 0.0}
+    full = p.mode == MODE_DARTREE_FULL
     for t in range(1, p.d + 1):
-        props = topk_np(X[b, t - 1], p.k).tolist()
+        shared = None if full else topk_np(X[b, t - 1], p.k).tolist()
         cands = []
         for r, path in enumerate(nodes[t - 1]):
             ptok = path[-1] if path else ctx1
+            if full:
+                # batch_propose(path, num_drafts=W): this path's own W best
+                # tokens under x + E[ptok] . F[v] over the whole vocabulary
+                g_all = p.F.astype(np.float64) @ p.E[ptok].astype(np.float64)
+                cond = X[b, t - 1] + g_all
+                order = np.lexsort((np.arange(p.V), -cond))
+                props = [int(v) for v in order if X[b, t - 1, v] != -math.inf][:W]
+            else:
+                props = shared
             for tok in props:
                 x = X[b, t - 1, tok]
                 if x == -math.inf:
                     continue
                 g = 0.0
-                if p.mode == MODE_DARTREE:
+                if p.mode != MODE_DART:
                     g = float(np.dot(p.E[ptok].astype(np.float64), p.F[tok].astype(np.float64)))
                 cands.append(((score[path] + x) + g, tok, r, path + (tok,)))
         cands.sort(key=lambda c: (-c[0], c[1], c[2]))

@@ -1,0 +1,162 @@
+"""Pins of the oracle's full-vocabulary DARTree mode: every frontier node
+proposes its own W tokens from the whole vocabulary under its
+parent-conditioned distribution x + E[parent] . F[v] (DARTree page, "Tree
+Construction": W candidate tokens per node, all candidates scored in one
+batch, top-W across the frontier), then the usual frontier and budget.
+
+Each pin checks the oracle against something other than itself: the page's
+sketch with per-path proposals, brute force over all one-step extensions,
+the reduction to DART mode when E = F = 0, the greedy decode at W = 1, the
+full V-ary trie, best-first selection restated over the full candidate tree,
+and the invariants of any correct tree.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from draft_tree_construction_dt_amd import synth
+from refcheck import (MODE_DART, MODE_DARTREE_FULL, NGRAM_DENSE_BIGRAM, NGRAM_NONE, all_valid_paths,
+                      check_invariants, has_near_ties, logits_f64, lse_np, paths_of, sketch_build)
+
+
+def _rand(seed, **kw):
+    rng = np.random.default_rng(seed)
+    args = dict(B=1, V=20, d=4, k=4, W=3, budget=12, mode=MODE_DARTREE_FULL, R=4)
+    args.update(kw)
+    return synth.random_problem(rng, **args)
+
+
+def _g(p, a, c):
+    return float(np.dot(p.E[a].astype(np.float64), p.F[c].astype(np.float64)))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_matches_sketch_with_per_path_proposals(oracle_lib, seed):
+    """The page's sketch with batch_propose(path, W) = that path's own W best
+    tokens over the vocabulary."""
+    W = 4
+    p = _rand(seed, V=24, d=5, W=W, budget=5 * W, integer_logits=(seed % 2 == 0))
+    out = oracle_lib.build_tree(p)
+    nodes = sketch_build(p, 0, W)
+    got = paths_of(out, 0)
+    by_depth = {}
+    for q in sorted(got, key=lambda q: got[q]):
+        by_depth.setdefault(len(q), []).append(q)
+    for t in range(1, p.d + 1):
+        assert by_depth.get(t, []) == nodes.get(t, []), f"depth {t}"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_bruteforce_top_w_of_all_extensions(oracle_lib, seed):
+    """Depth t is the top-W of ALL one-step extensions (every token of the
+    vocabulary) of depth t-1: taking each parent's W best first loses
+    nothing, since no parent contributes more than W to the top-W."""
+    p = _rand(seed, V=7, d=4, neg_inf_frac=0.1 * (seed % 3))
+    W = 3
+    out = oracle_lib.build_tree(p, W=W, budget=p.d * W)
+    paths = all_valid_paths(p, 0)
+    if has_near_ties([v[1] for v in paths.values()], 1e-9):
+        pytest.skip("near tie")
+    got = paths_of(out, 0)
+    prev = {()}
+    for t in range(1, p.d + 1):
+        ext = [q for q in paths if len(q) == t and q[:-1] in prev]
+        best = sorted(ext, key=lambda q: -paths[q][1])[:W]
+        have = {q for q in got if len(q) == t}
+        assert have == set(best), f"depth {t}"
+        prev = have
+        if not have:
+            break
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_zero_embeddings_reduce_to_dart_with_k_equal_w(oracle_lib, seed):
+    """E = F = 0: a node's W best tokens are its position's top-W, so the tree
+    is DART's with k = W (no N-gram)."""
+    p = _rand(seed, B=2, V=30, d=5, W=4, budget=14, dtype=synth.DTYPE_BF16 if seed % 2 else synth.DTYPE_F32)
+    p.E[:] = 0
+    p.F[:] = 0
+    a = oracle_lib.build_tree(p)
+    p.mode = MODE_DART
+    p.k = p.W
+    b = oracle_lib.build_tree(p)
+    for key in ("n_nodes", "tokens", "parents", "depths", "scores", "mask"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_width_one_is_the_greedy_decode(oracle_lib, seed):
+    """W = 1: each depth takes argmax_v x_t[v] + E[previous token] . F[v]
+    (lower id on ties), starting from the root token."""
+    p = _rand(seed, B=2, V=40, d=6, W=1, budget=6)
+    out = oracle_lib.build_tree(p)
+    X = logits_f64(p)
+    for b in range(p.B):
+        prev, want = int(p.ctx[b, 1]), []
+        for i in range(p.d):
+            cond = X[b, i] + p.F.astype(np.float64) @ p.E[prev].astype(np.float64)
+            v = int(np.argmax(cond))
+            want.append(v)
+            prev = v
+        assert out["tokens"][b][: p.d].tolist() == want
+        assert out["parents"][b][: p.d].tolist() == [-1] + list(range(p.d - 1))
+
+
+def test_wide_enough_gives_the_full_vocabulary_trie(oracle_lib):
+    """W >= V^d and a budget that fits: every path over the vocabulary,
+    sum_t V^t nodes, every inner node with V children."""
+    V, d = 3, 3
+    n = V + V ** 2 + V ** 3
+    p = _rand(5, V=V, d=d, k=V, W=V ** d, budget=n)
+    out = oracle_lib.build_tree(p)
+    assert out["n_nodes"][0] == n
+    kids = np.bincount(out["parents"][0][out["parents"][0] >= 0], minlength=n)
+    deep = out["depths"][0] < d
+    assert np.all(kids[deep] == V) and np.all(kids[~deep] == 0)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_budget_is_best_first_over_the_candidate_tree(oracle_lib, seed):
+    """A binding budget keeps what best-first selection over the full
+    candidate tree keeps: repeatedly the best node whose parent is taken, by
+    (S desc, depth asc, BFS index asc), S recomputed in float64 here."""
+    p = _rand(seed, V=16, d=4, W=4, budget=16)
+    full = oracle_lib.build_tree(p, budget=p.d * p.W)
+    out = oracle_lib.build_tree(p, budget=7)
+    X = logits_f64(p)
+    L = [lse_np(X[0, i]) for i in range(p.d)]
+    n = int(full["n_nodes"][0])
+    tok, par, dep = full["tokens"][0], full["parents"][0], full["depths"][0]
+    S = []
+    for i in range(n):
+        ptok = int(p.ctx[0, 1]) if par[i] < 0 else int(tok[par[i]])
+        base = S[par[i]] if par[i] >= 0 else 0.0
+        S.append((base + (X[0, dep[i] - 1, tok[i]] - L[dep[i] - 1])) + _g(p, ptok, int(tok[i])))
+    if has_near_ties(S, 1e-9):
+        pytest.skip("near tie")
+    taken = []
+    for _ in range(min(7, n)):
+        avail = [i for i in range(n) if i not in taken and (par[i] < 0 or par[i] in taken)]
+        taken.append(min(avail, key=lambda i: (-S[i], dep[i], i)))
+    want = {q for q, i in paths_of(full, 0).items() if i in taken}
+    assert set(paths_of(out, 0)) == want
+    assert out["n_nodes"][0] == len(taken)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_invariants(oracle_lib, seed):
+    p = _rand(100 + seed, B=3, V=25, d=5, W=4, budget=11 if seed % 2 else 20,
+              dtype=synth.DTYPE_BF16 if seed % 2 else synth.DTYPE_F32, neg_inf_frac=0.1 * (seed % 3))
+    out = oracle_lib.build_tree(p)
+    assert not check_invariants(p, out)
+
+
+def test_continuity_still_filters_when_a_table_is_given(oracle_lib):
+    """With a table, a node's proposals are its W best admissible tokens."""
+    p = _rand(3, V=12, d=3, W=3, budget=9, ngram=NGRAM_DENSE_BIGRAM, min_logp=-2.5, density=0.5)
+    out = oracle_lib.build_tree(p)
+    assert not check_invariants(p, out)
+    p2 = _rand(3, V=12, d=3, W=3, budget=9, ngram=NGRAM_NONE)
+    assert not check_invariants(p2, oracle_lib.build_tree(p2))
