@@ -22,7 +22,7 @@ _LIB_PATH = os.path.join(_HERE, "libdt.so")
 
 DT_OK, DT_ERR_INVALID_ARG, DT_ERR_UNSUPPORTED, DT_ERR_WORKSPACE, DT_ERR_HIP = 0, 1, 2, 3, 4
 DT_DTYPE_F32, DT_DTYPE_BF16 = 0, 1
-DT_MODE_DART, DT_MODE_DARTREE = 0, 1
+DT_MODE_DART, DT_MODE_DARTREE, DT_MODE_DARTREE_FULL = 0, 1, 2
 DT_NGRAM_NONE, DT_NGRAM_DENSE_BIGRAM, DT_NGRAM_CSR_BIGRAM, DT_NGRAM_HASH_TRIGRAM = 0, 1, 2, 3
 
 

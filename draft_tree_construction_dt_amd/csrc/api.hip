@@ -68,6 +68,21 @@ WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s) {
     w.off_tx = take(rows * k * 4);
     w.off_vmask = take((int64_t)p->B * w.n_ctx_cap * 4);
     w.off_g = take(p->mode == DT_MODE_DARTREE ? rows * k * k * 8 : 0);
+    const bool full = p->mode == DT_MODE_DARTREE_FULL;
+    const int64_t B = p->B, fw = full ? (int64_t)p->B * p->W : 0, nn = full ? fw * p->d : 0;
+    w.vchunk = kVocabChunk;
+    w.C2 = full ? (int)ceil_div(p->V, kVocabChunk) : 0;
+    w.off_f_tok = take(fw * 4);
+    w.off_f_rk = take(fw * 8);
+    w.off_f_s = take(fw * 8);
+    w.off_f_node = take(fw * 4);
+    w.off_f_n = take(full ? B * 4 : 0);
+    w.off_n_tree = take(full ? B * 4 : 0);
+    w.off_nd_tok = take(nn * 4);
+    w.off_nd_par = take(nn * 4);
+    w.off_nd_dep = take(nn * 4);
+    w.off_nd_s = take(nn * 8);
+    w.off_part = take(fw * w.C2 * (int64_t)sizeof(VocabEntry));
     w.total = (size_t)round_up(off, 256);
     return w;
 }
@@ -114,7 +129,8 @@ static dt_status check_shape(const dt_params* p) {
         return DT_ERR_INVALID_ARG;
     if (p->k > p->V) return DT_ERR_INVALID_ARG;
     if (p->dtype != DT_DTYPE_F32 && p->dtype != DT_DTYPE_BF16) return DT_ERR_INVALID_ARG;
-    if (p->mode != DT_MODE_DART && p->mode != DT_MODE_DARTREE) return DT_ERR_INVALID_ARG;
+    if (p->mode != DT_MODE_DART && p->mode != DT_MODE_DARTREE && p->mode != DT_MODE_DARTREE_FULL)
+        return DT_ERR_INVALID_ARG;
     if (p->sweep_chunks < 0) return DT_ERR_INVALID_ARG;
     if (p->d > kMaxD || p->k > kMaxK || p->W > kMaxW || p->budget > kMaxBudget ||
         p->W * p->k > kMaxCandidates || p->V >= kMaxV)
@@ -197,6 +213,101 @@ static dt_status launch_sweep_for(const void* logits, const dt_params* p, const 
     return DT_OK;
 }
 
+// Full-vocabulary DARTree mode: the sweep and the row merge give lse; then
+// per depth the vocabulary kernel and the frontier merge; then the budget
+// and the outputs.  The profiling events (if given) bracket the depth loop.
+static dt_status build_full(const void* logits, const dt_params* p, const SweepPlan& s, const WorkspacePlan& w,
+                            const dt_tree_out* out) {
+    hipStream_t stream = (hipStream_t)p->stream;
+    char* ws = (char*)p->workspace;
+    SweepArgs sa{};
+    sa.logits = logits;
+    sa.V = p->V;
+    sa.C = s.C;
+    sa.chunk = s.chunk;
+    sa.lists = s.lists;
+    sa.k = p->k;
+    sa.part_m = (float*)(ws + w.off_m);
+    sa.part_s = (double*)(ws + w.off_s);
+    sa.part_keys = (unsigned long long*)(ws + w.off_keys);
+    if (launch_sweep(sa, s.rows, p->dtype, stream) != hipSuccess) return DT_ERR_HIP;
+    MergeArgs ma{};
+    ma.rows = (int)s.rows;
+    ma.C = s.C * s.lists;
+    ma.k = p->k;
+    ma.part_m = sa.part_m;
+    ma.part_s = sa.part_s;
+    ma.part_keys = sa.part_keys;
+    ma.lse = (double*)(ws + w.off_lse);
+    ma.tok = (int32_t*)(ws + w.off_ttok);
+    ma.val = (float*)(ws + w.off_tx);
+    if (launch_merge(ma, stream) != hipSuccess) return DT_ERR_HIP;
+
+    VocabArgs va{};
+    va.B = p->B;
+    va.V = p->V;
+    va.d = p->d;
+    va.W = p->W;
+    va.R = p->R;
+    va.dtype = p->dtype;
+    va.vchunk = w.vchunk;
+    va.C2 = w.C2;
+    va.logits = logits;
+    va.E = p->E;
+    va.F = p->F;
+    va.ctx = p->ctx;
+    va.f_tok = (const int32_t*)(ws + w.off_f_tok);
+    va.f_rk = (const double*)(ws + w.off_f_rk);
+    va.f_n = (const int32_t*)(ws + w.off_f_n);
+    va.part = (VocabEntry*)(ws + w.off_part);
+    FrontierArgs fa{};
+    fa.B = p->B;
+    fa.d = p->d;
+    fa.W = p->W;
+    fa.C2 = w.C2;
+    fa.part = va.part;
+    fa.lse = ma.lse;
+    fa.f_tok = (int32_t*)(ws + w.off_f_tok);
+    fa.f_rk = (double*)(ws + w.off_f_rk);
+    fa.f_s = (double*)(ws + w.off_f_s);
+    fa.f_node = (int32_t*)(ws + w.off_f_node);
+    fa.f_n = (int32_t*)(ws + w.off_f_n);
+    fa.n_tree = (int32_t*)(ws + w.off_n_tree);
+    fa.nd_tok = (int32_t*)(ws + w.off_nd_tok);
+    fa.nd_par = (int32_t*)(ws + w.off_nd_par);
+    fa.nd_dep = (int32_t*)(ws + w.off_nd_dep);
+    fa.nd_s = (double*)(ws + w.off_nd_s);
+    if (p->prof_event_start && hipEventRecord((hipEvent_t)p->prof_event_start, stream) != hipSuccess)
+        return DT_ERR_HIP;
+    for (int t = 1; t <= p->d; ++t) {
+        va.t = t;
+        fa.t = t;
+        if (launch_vocab(va, stream) != hipSuccess) return DT_ERR_HIP;
+        if (launch_frontier(fa, stream) != hipSuccess) return DT_ERR_HIP;
+    }
+    if (p->prof_event_stop && hipEventRecord((hipEvent_t)p->prof_event_stop, stream) != hipSuccess)
+        return DT_ERR_HIP;
+    FinishArgs na{};
+    na.B = p->B;
+    na.d = p->d;
+    na.W = p->W;
+    na.budget = p->budget;
+    na.mask_words = (p->budget + 31) / 32;
+    na.n_tree = fa.n_tree;
+    na.nd_tok = fa.nd_tok;
+    na.nd_par = fa.nd_par;
+    na.nd_dep = fa.nd_dep;
+    na.nd_s = fa.nd_s;
+    na.n_nodes = out->n_nodes;
+    na.tokens = out->tokens;
+    na.parents = out->parents;
+    na.depths = out->depths;
+    na.scores = out->scores;
+    na.mask = out->mask;
+    if (launch_finish(na, stream) != hipSuccess) return DT_ERR_HIP;
+    return DT_OK;
+}
+
 extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngram,
                                    const dt_params* p, const dt_tree_out* out) {
     dt_status st = check_shape(p);
@@ -208,6 +319,12 @@ extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngr
         if (p->R < 4 || p->R > 256 || p->R % 4 != 0) return DT_ERR_UNSUPPORTED;
         if (((uintptr_t)p->E & 15u) || ((uintptr_t)p->F & 15u)) return DT_ERR_INVALID_ARG;
     }
+    if (p->mode == DT_MODE_DARTREE_FULL) {
+        if (!p->E || !p->F) return DT_ERR_INVALID_ARG;
+        if (((uintptr_t)p->E & 15u) || ((uintptr_t)p->F & 15u)) return DT_ERR_INVALID_ARG;
+        if (p->R != 16 && p->R != 32 && p->R != 64) return DT_ERR_UNSUPPORTED;
+        if (p->W > kFullMaxW || ngram->kind != DT_NGRAM_NONE) return DT_ERR_UNSUPPORTED;
+    }
     const TreePlan plan = plan_tree(p, ngram->kind);
     if (plan.total > kTreeLdsLimit) return DT_ERR_UNSUPPORTED;
     if (p->B == 0) return DT_OK;
@@ -218,6 +335,7 @@ extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngr
 
     const SweepPlan s = plan_sweep(p);
     const WorkspacePlan w = plan_workspace(p, s);
+    if (p->mode == DT_MODE_DARTREE_FULL) return build_full(logits, p, s, w, out);
     if ((st = launch_sweep_for(logits, p, s, w)) != DT_OK) return st;
 
     char* ws = (char*)p->workspace;

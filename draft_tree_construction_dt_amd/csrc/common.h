@@ -64,9 +64,19 @@ struct SweepPlan {
 //   tx        float  [rows][k]        their logits
 //   vmask     uint32 [B][n_ctx_cap]   admissible children of every context
 //   g         double [rows][k][k]     parent-conditioned terms (DARTree only)
+//   full-vocabulary DARTree mode only:
+//   f_tok, f_rk, f_s, f_node  [B][W]     the current frontier: token, Rk, S, node index
+//   f_n, n_tree               [B]        frontier size, candidate-tree size
+//   nd_tok, nd_par, nd_dep    [B][d*W]   candidate-tree nodes in BFS order
+//   nd_s                      [B][d*W]   their cumulative log-scores
+//   part                      [B][C2][W] each vocabulary chunk's top-W (VocabEntry)
 struct WorkspacePlan {
-    size_t off_m, off_s, off_keys, off_lse, off_ttok, off_tx, off_vmask, off_g, total;
+    size_t off_m, off_s, off_keys, off_lse, off_ttok, off_tx, off_vmask, off_g;
+    size_t off_f_tok, off_f_rk, off_f_s, off_f_node, off_f_n, off_n_tree;
+    size_t off_nd_tok, off_nd_par, off_nd_dep, off_nd_s, off_part;
+    size_t total;
     int n_ctx_cap;      // contexts per request the vmask area holds (the trigram count)
+    int vchunk, C2;     // full-vocabulary mode: columns per chunk and chunk count
 };
 
 // Shared-memory plan of the tree kernel (byte offsets into dynamic LDS).
@@ -160,6 +170,70 @@ struct NGramUpdateArgs {
     int* counts;
 };
 
+// ---------------------------------------------------------------------------
+// Full-vocabulary DARTree mode: per depth, every frontier node scores every
+// token v by Rk = (Rk_parent + x[v]) + E[parent_tok] . F[v].
+// ---------------------------------------------------------------------------
+constexpr int kVocabReqPerWave = 2;                       // requests a wave owns
+constexpr int kVocabReqPerGroup = kVocabReqPerWave * kWaves;
+constexpr int kVocabCap = 320;                            // per-(wave, request) candidate buffer
+constexpr int kVocabChunk = 256;                          // vocabulary columns per workgroup
+constexpr int kFullMaxW = 16;                             // one 16-row MFMA tile per request
+
+// one entry of a chunk's top-W list: exact key, the parent-conditioned term,
+// the logit and the tie key token * 64 + parent rank (smaller wins)
+struct VocabEntry {
+    double rk;
+    double g;
+    float x;
+    uint32_t tie;
+    uint32_t pad[2];
+};
+
+struct VocabArgs {
+    int B, V, d, W, R, t, dtype;
+    int vchunk, C2;
+    const void* logits;
+    const float* E;
+    const float* F;
+    const int32_t* ctx;
+    const int32_t* f_tok;
+    const double* f_rk;
+    const int32_t* f_n;
+    VocabEntry* part;
+};
+
+struct FrontierArgs {
+    int B, d, W, t, C2;
+    const VocabEntry* part;
+    const double* lse;
+    int32_t* f_tok;
+    double* f_rk;
+    double* f_s;
+    int32_t* f_node;
+    int32_t* f_n;
+    int32_t* n_tree;
+    int32_t* nd_tok;
+    int32_t* nd_par;
+    int32_t* nd_dep;
+    double* nd_s;
+};
+
+struct FinishArgs {
+    int B, d, W, budget, mask_words;
+    const int32_t* n_tree;
+    const int32_t* nd_tok;
+    const int32_t* nd_par;
+    const int32_t* nd_dep;
+    const double* nd_s;
+    int32_t* n_nodes;
+    int32_t* tokens;
+    int32_t* parents;
+    int32_t* depths;
+    float* scores;
+    uint32_t* mask;
+};
+
 struct MergeArgs {
     int rows, C, k;
     const float* part_m;
@@ -182,5 +256,8 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_ngram_update(const NGramUpdateArgs& a, hipStream_t stream);
+hipError_t launch_vocab(const VocabArgs& a, hipStream_t stream);
+hipError_t launch_frontier(const FrontierArgs& a, hipStream_t stream);
+hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
 
 }  // namespace dt

@@ -18,7 +18,15 @@
 // one by one in any order, as long as no row fills up and no probe sequence
 // runs out of free slots; which slot a key added in the same call lands in,
 // and which successors survive a row that overflows, depend on timing.
-// Reads of entries other threads may claim use device-scope atomic loads.
+//
+// Latency, not bandwidth, bounds this kernel (a few hundred trigrams per
+// call, each a chain of dependent memory round trips), so each round trip
+// covers eight slots or entries: plain loads of an aligned group, then the
+// scan in registers.  A plain load may return an entry's old value while
+// another workgroup (on another XCD's L2) is claiming it; since an entry only
+// ever goes from free to a value, the stale value can only be "free", and
+// the CAS that follows returns the real one.  The counters are summed per
+// wave before one atomic add each.
 #include "common.h"
 
 namespace dt {
@@ -33,60 +41,102 @@ __device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
     return z ^ (z >> 31);
 }
 
+// Find or claim the slot of `key`: its index, or -1 if the whole probe
+// sequence is taken by other keys.  *added is set when this thread claimed it.
+__device__ __forceinline__ long long find_or_claim(unsigned long long* keys, long long cap,
+                                                   unsigned long long key, int* added) {
+    const unsigned long long cm = (unsigned long long)cap - 1ull;
+    const int G = cap < 8 ? (int)cap : 8;                   // cap is a power of two
+    const unsigned long long pos = mix64(key) & cm;
+    unsigned long long g0 = pos & ~(unsigned long long)(G - 1);
+    int off = (int)(pos - g0);
+    long long slot = -1;
+    for (long long seen = 0; seen < cap && slot < 0; seen += G - off, off = 0, g0 = (g0 + G) & cm) {
+        unsigned long long v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = j < G ? keys[g0 + j] : 0ull;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (slot >= 0 || j < off || j >= G) continue;
+            if (v[j] == key) {
+                slot = (long long)(g0 + j);
+            } else if (v[j] == kFree) {
+                const unsigned long long cur = atomicCAS(keys + g0 + j, kFree, key);
+                if (cur == kFree) *added = 1;
+                if (cur == kFree || cur == key) slot = (long long)(g0 + j);
+            }
+        }
+    }
+    return slot;
+}
+
+// Add successor c to a row of S entries.  1 = added at entry *at, 0 = present
+// already, -1 = the row is full of other successors.  A row whose slot this
+// thread has just claimed starts empty, so its first group is taken as free
+// without a load: the CAS returns what other threads may have put there.
+__device__ __forceinline__ int add_successor(int32_t* row, int S, int32_t c, int* at, bool fresh) {
+    for (int e0 = 0; e0 < S; e0 += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = e0 + j >= S ? 0 : (fresh && e0 == 0) ? -1 : row[e0 + j];
+        int res = -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (res >= 0 || e0 + j >= S) continue;
+            if (v[j] == c) {
+                res = 0;
+            } else if (v[j] == -1) {
+                const int32_t cur = atomicCAS(row + e0 + j, -1, c);
+                if (cur == -1) {
+                    res = 1;
+                    *at = e0 + j;
+                } else if (cur == c) {
+                    res = 0;
+                }
+            }
+        }
+        if (res >= 0) return res;
+    }
+    return -1;
+}
+
 __global__ void __launch_bounds__(kThreads) ngram_update_kernel(NGramUpdateArgs a) {
     const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (t >= (int64_t)a.B * a.L) return;
-    const int b = (int)(t / a.L), i = (int)(t - (int64_t)b * a.L);
-    const int n = a.lengths[b] < a.L ? a.lengths[b] : a.L;
-    if (i >= n) return;
-    const int32_t* tok = a.tokens + (int64_t)b * a.L;
-    const int32_t c = tok[i];
-    const int32_t t2 = i >= 2 ? tok[i - 2] : (i == 1 ? a.ctx[2 * b + 1] : a.ctx[2 * b]);
-    const int32_t t1 = i >= 1 ? tok[i - 1] : a.ctx[2 * b + 1];
-    const unsigned long long key = ((unsigned long long)(uint32_t)t2 << 32) | (uint32_t)t1;
-    int* counts = a.counts;
-    if (key == kFree) {                                       // indistinguishable from a free slot
-        if (counts) atomicAdd(&counts[2], 1);
-        return;
+    int key_added = 0, succ_added = 0, dropped = 0;
+    bool active = t < (int64_t)a.B * a.L;
+    unsigned long long key = 0;
+    int32_t c = 0;
+    if (active) {
+        // the length and the three tokens are independent loads, all in bounds
+        const int b = (int)(t / a.L), i = (int)(t - (int64_t)b * a.L);
+        const int32_t* tok = a.tokens + (int64_t)b * a.L;
+        const int len = a.lengths[b];
+        c = tok[i];
+        const int32_t t2 = i >= 2 ? tok[i - 2] : (i == 1 ? a.ctx[2 * b + 1] : a.ctx[2 * b]);
+        const int32_t t1 = i >= 1 ? tok[i - 1] : a.ctx[2 * b + 1];
+        key = ((unsigned long long)(uint32_t)t2 << 32) | (uint32_t)t1;
+        active = i < len;
     }
-    const unsigned long long cm = (unsigned long long)a.cap - 1ull;
-    unsigned long long pos = mix64(key) & cm;
-    long long slot = -1;
-    for (long long probe = 0; probe < a.cap; ++probe) {
-        unsigned long long* kp = a.keys + pos;
-        unsigned long long cur = __hip_atomic_load(kp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (cur == kFree) {
-            cur = atomicCAS(kp, kFree, key);
-            if (cur == kFree) {
-                if (counts) atomicAdd(&counts[0], 1);
-                slot = (long long)pos;
-                break;
-            }
+    if (active) {
+        const long long slot = key == kFree ? -1 : find_or_claim(a.keys, a.cap, key, &key_added);
+        if (slot < 0) {                                       // the free marker, or no free slot on the way
+            dropped = 1;
+        } else {
+            int at = 0;
+            const int r = add_successor(a.succ + slot * a.S, a.S, c, &at, key_added != 0);
+            if (r > 0 && a.hash_logp) a.hash_logp[slot * a.S + at] = a.new_logp;
+            succ_added = r > 0;
+            dropped = r < 0;
         }
-        if (cur == key) {
-            slot = (long long)pos;
-            break;
+    }
+    if (a.counts) {
+        const unsigned long long m0 = __ballot(key_added), m1 = __ballot(succ_added), m2 = __ballot(dropped);
+        if ((threadIdx.x & 63) == 0) {
+            if (m0) atomicAdd(&a.counts[0], __popcll(m0));
+            if (m1) atomicAdd(&a.counts[1], __popcll(m1));
+            if (m2) atomicAdd(&a.counts[2], __popcll(m2));
         }
-        pos = (pos + 1ull) & cm;
     }
-    if (slot < 0) {                                           // no free slot on the way
-        if (counts) atomicAdd(&counts[2], 1);
-        return;
-    }
-    int32_t* row = a.succ + slot * a.S;
-    for (int e = 0; e < a.S; ++e) {
-        int32_t cur = __hip_atomic_load(row + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (cur == -1) {
-            cur = atomicCAS(row + e, -1, c);
-            if (cur == -1) {
-                if (a.hash_logp) a.hash_logp[slot * a.S + e] = a.new_logp;
-                if (counts) atomicAdd(&counts[1], 1);
-                return;
-            }
-        }
-        if (cur == c) return;                                 // present already
-    }
-    if (counts) atomicAdd(&counts[2], 1);                     // row full
 }
 
 }  // namespace

@@ -532,6 +532,188 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
     }
 }
 
+// Steps 5 and 6 on a candidate tree of nb nodes held in LDS in BFS order
+// (tokens, parents as node indices, depths, cumulative scores).  `literal`
+// replays best-first one node at a time (scores may rise along a path);
+// otherwise S never rises along a path and the top-budget nodes by (S desc,
+// BFS index asc) are already closed under parents.
+struct EmitOut {
+    int32_t* n_nodes;
+    int32_t* tokens;
+    int32_t* parents;
+    int32_t* depths;
+    float* scores;
+    uint32_t* mask;
+    int budget;
+    int mask_words;
+};
+
+__device__ __forceinline__ void budget_and_emit(int nb, bool literal, int b, const int* n_tok, const int* n_par,
+                                                const int* n_dep, const double* n_s, int* n_new, int* n_out,
+                                                int* misc, const EmitOut& eo) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int budget = eo.budget;
+    // ---- 5. verification budget
+    int n_sel = nb;
+    if (nb <= budget) {
+        for (int i = tid; i < nb; i += kTreeThreads) {
+            n_new[i] = i;
+            n_out[i] = i;
+        }
+        __syncthreads();
+    } else if (!literal) {
+        // parent-closed top-budget by (S desc, BFS index asc)
+        const int per = (nb + kTreeThreads - 1) / kTreeThreads;
+        int flags = 0, cntl = 0;
+        for (int q = 0; q < per; ++q) {
+            const int i = tid * per + q;
+            if (i < nb) {
+                int r = 0;
+                const double si = n_s[i];
+                for (int j = 0; j < nb; ++j) r += node_before(n_s[j], j, si, i);
+                if (r < budget) {
+                    flags |= 1 << q;
+                    ++cntl;
+                }
+            }
+        }
+        int total;
+        int pos = block_exclusive_scan(cntl, misc + 16, &total);
+        for (int q = 0; q < per; ++q) {
+            const int i = tid * per + q;
+            if (i < nb) {
+                if (flags >> q & 1) {
+                    n_new[i] = pos;
+                    n_out[pos] = i;
+                    ++pos;
+                } else {
+                    n_new[i] = -1;
+                }
+            }
+        }
+        n_sel = total;
+        __syncthreads();
+    } else {
+        // best-first, literally: take the best available node budget times
+        for (int i = tid; i < nb; i += kTreeThreads) n_new[i] = (n_par[i] < 0) ? -2 : -3;  // -2 available, -3 waiting
+        __syncthreads();
+        if (wave == 0) {
+            for (int step = 0; step < budget; ++step) {
+                double bs = -INFINITY;
+                int bi = -1;
+                for (int i = lane; i < nb; i += 64)
+                    if (n_new[i] == -2 && (bi < 0 || node_before(n_s[i], i, bs, bi))) {
+                        bs = n_s[i];
+                        bi = i;
+                    }
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) {
+                    const double os = __shfl_xor(bs, off);
+                    const int oi = __shfl_xor(bi, off);
+                    if (oi >= 0 && (bi < 0 || node_before(os, oi, bs, bi))) {
+                        bs = os;
+                        bi = oi;
+                    }
+                }
+                if (bi < 0) break;                                // cannot happen: nb > budget
+                __builtin_amdgcn_wave_barrier();
+                if (lane == 0) n_new[bi] = -1;                    // taken (index assigned below)
+                __builtin_amdgcn_wave_barrier();
+                for (int i = lane; i < nb; i += 64)
+                    if (n_par[i] == bi) n_new[i] = -2;
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+        __syncthreads();
+        // taken nodes keep BFS order
+        const int per = (nb + kTreeThreads - 1) / kTreeThreads;
+        int cntl = 0;
+        for (int q = 0; q < per; ++q) {
+            const int i = tid * per + q;
+            if (i < nb && n_new[i] == -1) ++cntl;
+        }
+        int total;
+        int pos = block_exclusive_scan(cntl, misc + 16, &total);
+        __syncthreads();
+        for (int q = 0; q < per; ++q) {
+            const int i = tid * per + q;
+            if (i < nb) {
+                if (n_new[i] == -1) {
+                    n_new[i] = pos;
+                    n_out[pos] = i;
+                    ++pos;
+                } else {
+                    n_new[i] = -1;
+                }
+            }
+        }
+        n_sel = total;
+        __syncthreads();
+    }
+
+    // ---- 6. outputs in BFS order, parents remapped, ancestor mask
+    const int64_t ob = (int64_t)b * budget;
+    for (int o = tid; o < budget; o += kTreeThreads) {
+        if (o < n_sel) {
+            const int i = n_out[o];
+            eo.tokens[ob + o] = n_tok[i];
+            eo.parents[ob + o] = n_par[i] < 0 ? -1 : n_new[n_par[i]];
+            eo.depths[ob + o] = n_dep[i];
+            eo.scores[ob + o] = (float)n_s[i];
+        } else {
+            eo.tokens[ob + o] = -1;
+            eo.parents[ob + o] = -1;
+            eo.depths[ob + o] = 0;
+            eo.scores[ob + o] = -INFINITY;
+        }
+    }
+    const int words = eo.mask_words;
+    if (budget * words > kTreeThreads && words <= 8) {
+        // more (node, word) pairs than threads: one thread per node walks its
+        // ancestors once and sets their bits in all its words
+        for (int o = tid; o < budget; o += kTreeThreads) {
+            uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0, a4 = 0, a5 = 0, a6 = 0, a7 = 0;
+            if (o < n_sel) {
+                for (int i = n_out[o]; i >= 0; i = n_par[i]) {
+                    const int ni = n_new[i];
+                    const uint32_t bit = 1u << (ni & 31), wd = (uint32_t)ni >> 5;
+                    a0 |= wd == 0 ? bit : 0u;
+                    a1 |= wd == 1 ? bit : 0u;
+                    a2 |= wd == 2 ? bit : 0u;
+                    a3 |= wd == 3 ? bit : 0u;
+                    a4 |= wd == 4 ? bit : 0u;
+                    a5 |= wd == 5 ? bit : 0u;
+                    a6 |= wd == 6 ? bit : 0u;
+                    a7 |= wd == 7 ? bit : 0u;
+                }
+            }
+            uint32_t* row = eo.mask + (ob + o) * words;
+            row[0] = a0;
+            if (words > 1) row[1] = a1;
+            if (words > 2) row[2] = a2;
+            if (words > 3) row[3] = a3;
+            if (words > 4) row[4] = a4;
+            if (words > 5) row[5] = a5;
+            if (words > 6) row[6] = a6;
+            if (words > 7) row[7] = a7;
+        }
+    } else {
+        for (int e = tid; e < budget * words; e += kTreeThreads) {
+            const int o = e / words, w = e - o * words;
+            uint32_t bits = 0;
+            if (o < n_sel) {
+                for (int i = n_out[o]; i >= 0; i = n_par[i]) {
+                    const int ni = n_new[i];
+                    if ((ni >> 5) == w) bits |= 1u << (ni & 31);
+                }
+            }
+            eo.mask[ob * words + e] = bits;
+        }
+    }
+    if (tid == 0) eo.n_nodes[b] = n_sel;
+}
+
 template <int RM>
 __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -781,164 +963,34 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     __syncthreads();
     nb = misc[0];                                            // ordered by the barrier
 
-    // ---- 5. verification budget
-    int n_sel = nb;
-    if (nb <= budget) {
-        for (int i = tid; i < nb; i += kTreeThreads) {
-            n_new[i] = i;
-            n_out[i] = i;
-        }
-        __syncthreads();
-    } else if (!dartree) {
-        // parent-closed top-budget by (S desc, BFS index asc)
-        const int per = (nb + kTreeThreads - 1) / kTreeThreads;
-        int flags = 0, cntl = 0;
-        for (int q = 0; q < per; ++q) {
-            const int i = tid * per + q;
-            if (i < nb) {
-                int r = 0;
-                const double si = n_s[i];
-                for (int j = 0; j < nb; ++j) r += node_before(n_s[j], j, si, i);
-                if (r < budget) {
-                    flags |= 1 << q;
-                    ++cntl;
-                }
-            }
-        }
-        int total;
-        int pos = block_exclusive_scan(cntl, misc + 16, &total);
-        for (int q = 0; q < per; ++q) {
-            const int i = tid * per + q;
-            if (i < nb) {
-                if (flags >> q & 1) {
-                    n_new[i] = pos;
-                    n_out[pos] = i;
-                    ++pos;
-                } else {
-                    n_new[i] = -1;
-                }
-            }
-        }
-        n_sel = total;
-        __syncthreads();
-    } else {
-        // best-first, literally: take the best available node budget times
-        for (int i = tid; i < nb; i += kTreeThreads) n_new[i] = (n_par[i] < 0) ? -2 : -3;  // -2 available, -3 waiting
-        __syncthreads();
-        if (wave == 0) {
-            for (int step = 0; step < budget; ++step) {
-                double bs = -INFINITY;
-                int bi = -1;
-                for (int i = lane; i < nb; i += 64)
-                    if (n_new[i] == -2 && (bi < 0 || node_before(n_s[i], i, bs, bi))) {
-                        bs = n_s[i];
-                        bi = i;
-                    }
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) {
-                    const double os = __shfl_xor(bs, off);
-                    const int oi = __shfl_xor(bi, off);
-                    if (oi >= 0 && (bi < 0 || node_before(os, oi, bs, bi))) {
-                        bs = os;
-                        bi = oi;
-                    }
-                }
-                if (bi < 0) break;                                // cannot happen: nb > budget
-                __builtin_amdgcn_wave_barrier();
-                if (lane == 0) n_new[bi] = -1;                    // taken (index assigned below)
-                __builtin_amdgcn_wave_barrier();
-                for (int i = lane; i < nb; i += 64)
-                    if (n_par[i] == bi) n_new[i] = -2;
-                __builtin_amdgcn_wave_barrier();
-            }
-        }
-        __syncthreads();
-        // taken nodes keep BFS order
-        const int per = (nb + kTreeThreads - 1) / kTreeThreads;
-        int cntl = 0;
-        for (int q = 0; q < per; ++q) {
-            const int i = tid * per + q;
-            if (i < nb && n_new[i] == -1) ++cntl;
-        }
-        int total;
-        int pos = block_exclusive_scan(cntl, misc + 16, &total);
-        __syncthreads();
-        for (int q = 0; q < per; ++q) {
-            const int i = tid * per + q;
-            if (i < nb) {
-                if (n_new[i] == -1) {
-                    n_new[i] = pos;
-                    n_out[pos] = i;
-                    ++pos;
-                } else {
-                    n_new[i] = -1;
-                }
-            }
-        }
-        n_sel = total;
-        __syncthreads();
-    }
+    budget_and_emit(nb, dartree, b, n_tok, n_par, n_dep, n_s, n_new, n_out, misc,
+                    EmitOut{a.n_nodes, a.tokens, a.parents, a.depths, a.scores, a.mask, budget, a.mask_words});
+}
 
-    // ---- 6. outputs in BFS order, parents remapped, ancestor mask
-    const int64_t ob = (int64_t)b * budget;
-    for (int o = tid; o < budget; o += kTreeThreads) {
-        if (o < n_sel) {
-            const int i = n_out[o];
-            a.tokens[ob + o] = n_tok[i];
-            a.parents[ob + o] = n_par[i] < 0 ? -1 : n_new[n_par[i]];
-            a.depths[ob + o] = n_dep[i];
-            a.scores[ob + o] = (float)n_s[i];
-        } else {
-            a.tokens[ob + o] = -1;
-            a.parents[ob + o] = -1;
-            a.depths[ob + o] = 0;
-            a.scores[ob + o] = -INFINITY;
-        }
+// Full-vocabulary DARTree mode: the candidate tree the frontier kernels built
+// (workspace, BFS order) goes through the same budget and output stages.
+__global__ void __launch_bounds__(kTreeThreads) finish_kernel(FinishArgs a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int nmax = a.d * a.W;
+    double* n_s = reinterpret_cast<double*>(lds);
+    int* n_tok = reinterpret_cast<int*>(n_s + nmax);
+    int* n_par = n_tok + nmax;
+    int* n_dep = n_par + nmax;
+    int* n_new = n_dep + nmax;
+    int* n_out = n_new + nmax;
+    int* misc = n_out + nmax;
+    const int nb = a.n_tree[b];
+    const int64_t src = (int64_t)b * nmax;
+    for (int i = tid; i < nb; i += kTreeThreads) {
+        n_s[i] = a.nd_s[src + i];
+        n_tok[i] = a.nd_tok[src + i];
+        n_par[i] = a.nd_par[src + i];
+        n_dep[i] = a.nd_dep[src + i];
     }
-    const int words = a.mask_words;
-    if (budget * words > kTreeThreads && words <= 8) {
-        // more (node, word) pairs than threads: one thread per node walks its
-        // ancestors once and sets their bits in all its words
-        for (int o = tid; o < budget; o += kTreeThreads) {
-            uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0, a4 = 0, a5 = 0, a6 = 0, a7 = 0;
-            if (o < n_sel) {
-                for (int i = n_out[o]; i >= 0; i = n_par[i]) {
-                    const int ni = n_new[i];
-                    const uint32_t bit = 1u << (ni & 31), wd = (uint32_t)ni >> 5;
-                    a0 |= wd == 0 ? bit : 0u;
-                    a1 |= wd == 1 ? bit : 0u;
-                    a2 |= wd == 2 ? bit : 0u;
-                    a3 |= wd == 3 ? bit : 0u;
-                    a4 |= wd == 4 ? bit : 0u;
-                    a5 |= wd == 5 ? bit : 0u;
-                    a6 |= wd == 6 ? bit : 0u;
-                    a7 |= wd == 7 ? bit : 0u;
-                }
-            }
-            uint32_t* row = a.mask + (ob + o) * words;
-            row[0] = a0;
-            if (words > 1) row[1] = a1;
-            if (words > 2) row[2] = a2;
-            if (words > 3) row[3] = a3;
-            if (words > 4) row[4] = a4;
-            if (words > 5) row[5] = a5;
-            if (words > 6) row[6] = a6;
-            if (words > 7) row[7] = a7;
-        }
-    } else {
-        for (int e = tid; e < budget * words; e += kTreeThreads) {
-            const int o = e / words, w = e - o * words;
-            uint32_t bits = 0;
-            if (o < n_sel) {
-                for (int i = n_out[o]; i >= 0; i = n_par[i]) {
-                    const int ni = n_new[i];
-                    if ((ni >> 5) == w) bits |= 1u << (ni & 31);
-                }
-            }
-            a.mask[ob * words + e] = bits;
-        }
-    }
-    if (tid == 0) a.n_nodes[b] = n_sel;
+    __syncthreads();
+    budget_and_emit(nb, true, b, n_tok, n_par, n_dep, n_s, n_new, n_out, misc,
+                    EmitOut{a.n_nodes, a.tokens, a.parents, a.depths, a.scores, a.mask, a.budget, a.mask_words});
 }
 
 // one wave per row: per-position normaliser and top-k only
@@ -977,6 +1029,14 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(tree_kernel<4>, dim3((unsigned)a.B), dim3(kTreeThreads), (size_t)a.plan.total, stream, a);
     else
         hipLaunchKernelGGL(tree_kernel<16>, dim3((unsigned)a.B), dim3(kTreeThreads), (size_t)a.plan.total, stream, a);
+    return hipGetLastError();
+}
+
+static size_t finish_lds_bytes(int d, int W) { return (size_t)d * W * (8 + 5 * 4) + kMiscInts * 4; }
+
+hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {
+    if (a.B <= 0) return hipSuccess;
+    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)a.B), dim3(kTreeThreads), finish_lds_bytes(a.d, a.W), stream, a);
     return hipGetLastError();
 }
 

@@ -41,6 +41,18 @@
  *      `budget` nodes are taken.
  *   5. Output in BFS order (depth asc, then frontier rank).
  *
+ * DARTREE_FULL mode (DARTree page, "Tree Construction": the drafter proposes
+ * W candidate tokens per frontier node): instead of the position's shared
+ * top-k, every frontier node p proposes its own W best tokens of the whole
+ * vocabulary under its parent-conditioned distribution x[v] + E[tok_p].F[v]
+ * (order: Rk desc, token asc), and the frontier is the top-W of all
+ * proposals, ranked as in step 3.  This equals the top-W over every
+ * (node, token) pair.  k is not used for proposals; the N-gram table must
+ * be of kind NONE; W <= 16 and R in {16, 32, 64}.  Keys are exact fp64 (the
+ * dense product runs on fp32 matrix cores only to discard tokens that
+ * provably cannot be selected).  Best-first selection is replayed literally
+ * (g may be positive, so S can rise along a path).
+ *
  * Output tree (caller-allocated device memory, n_max = budget,
  * mask_words = ceil(budget / 32)):
  *   n_nodes [B]                     int32, number of draft nodes (0..budget)
@@ -100,7 +112,8 @@ typedef enum dt_dtype { DT_DTYPE_F32 = 0, DT_DTYPE_BF16 = 1 } dt_dtype;
 
 typedef enum dt_mode {
     DT_MODE_DART = 0,      /* score = cumulative draft log-probability */
-    DT_MODE_DARTREE = 1    /* + parent-conditioned term E[parent] . F[child] */
+    DT_MODE_DARTREE = 1,   /* + parent-conditioned term E[parent] . F[child] */
+    DT_MODE_DARTREE_FULL = 2  /* DARTREE with per-node proposals over the whole vocabulary */
 } dt_mode;
 
 typedef enum dt_ngram_kind {
@@ -172,11 +185,13 @@ dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngram,
                         const dt_params* params, const dt_tree_out* out);
 
 /* Bytes of workspace dt_build_tree / dt_position_topk need for these
- * parameters (depends on B, V, d, k, mode, dtype and sweep_chunks only; the
- * N-gram area is sized for the largest table kind); 0 if the parameters are
- * invalid.  The workspace holds the sweep's per-chunk partials and the
- * per-row normalisers, top-k lists, continuity masks (and DARTree terms)
- * the tree step reads; its contents are meaningless between calls. */
+ * parameters (depends on B, V, d, k, mode, dtype and sweep_chunks only, and
+ * on W in DARTREE_FULL mode; the N-gram area is sized for the largest table
+ * kind); 0 if the parameters are invalid.  The workspace holds the sweep's
+ * per-chunk partials and the per-row normalisers, top-k lists, continuity
+ * masks (and DARTree terms) the tree step reads; in DARTREE_FULL mode also
+ * the frontier, the candidate tree and every vocabulary chunk's top-W.  Its
+ * contents are meaningless between calls. */
 size_t dt_workspace_size(const dt_params* params);
 
 /* Static, human-readable name of a status code. */
