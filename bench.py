@@ -63,7 +63,7 @@ def parse():
     ap.add_argument("--sweep-chunks", type=int, default=0, help="0 = the library's automatic plan")
     ap.add_argument("--workload", default="c4p",
                     help="c4p (the default JSON contract) or another named configuration, timed per call "
-                         "(c1, c2, c2p, c3, c3p, c4, c4L, c4Lp, c5)")
+                         "(c1, c2, c2p, c3, c3p, c4, c4L, c4Lp, c5, c5f)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -157,6 +157,7 @@ def run_workload(args) -> None:
     to exceed the Infinity Cache where the generator allows it (small
     configurations stay cache-resident and are latency-bound anyway)."""
     import statistics
+    import numpy as np
     import torch
     from draft_tree_construction_dt_amd import binding as bd, synth
 
@@ -173,7 +174,7 @@ def run_workload(args) -> None:
     ctx = torch.from_numpy(prob.ctx).to(dev)
     ngram = bd.upload_ngram(prob.ngram, dev)
     E = F = None
-    if prob.mode == bd.DT_MODE_DARTREE:
+    if prob.mode != bd.DT_MODE_DART:
         E = torch.from_numpy(prob.E).to(dev)
         F = torch.from_numpy(prob.F).to(dev)
     stream = torch.cuda.current_stream()
@@ -211,6 +212,41 @@ def run_workload(args) -> None:
         tev.destroy(a)
         tev.destroy(b)
     med = statistics.median(us)
+    full = None
+    if prob.mode == bd.DT_MODE_DARTREE_FULL:
+        # the depth loop alone (d vocabulary launches + d frontier merges),
+        # timed by events the library records around it on its stream
+        evs = [(tev.create(), tev.create()) for _ in range(K)]
+        for i in range(K):
+            pc = pcs[i % sets]
+            pc.prof_event_start, pc.prof_event_stop = evs[i]
+            fn(ptrs[i % sets], ctypes.byref(ng_c), ctypes.byref(pc), ctypes.byref(out_c))
+        torch.cuda.synchronize()
+        loop_us = sorted(tev.elapsed_ms(a, b) * 1e3 for a, b in evs)
+        for pc in pcs:
+            pc.prof_event_start = pc.prof_event_stop = None
+        for a, b in evs:
+            tev.destroy(a)
+            tev.destroy(b)
+        # algorithmic MFMA work: 2 R V flops per (frontier node, depth); the
+        # last call's tree (budget = d W keeps every node) gives the frontier
+        # sizes; 16-row tiles padded past the frontier are not counted
+        o = out.numpy()
+        R = prob.E.shape[1]
+        rows = 0
+        for b in range(cfg.B):
+            dep = o["depths"][b][: int(o["n_nodes"][b])]
+            rows += 1 + int(np.sum(dep < prob.d))
+        flops = 2.0 * R * prob.V * rows
+        lmed = statistics.median(loop_us)
+        full = {
+            "bound": "mfma", "kernel": "vocab_kernel + frontier_kernel, the whole depth loop",
+            "achieved": flops / lmed / 1e6, "peak": 157.3, "unit": "TFLOP/s",
+            "frac": flops / lmed / 1e6 / 157.3, "traffic": None,
+            "depth_loop_us_median": lmed, "algorithmic_flops_per_call": flops,
+            "timing": "HIP events recorded by the library around the depth loop, one stream",
+            "dtype": "fp32 MFMA for the bound, fp64 exact rescoring",
+        }
     res = {
         "metric": METRIC, "workload": args.workload, "value": cfg.B / med * 1e6, "unit": "trees/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "B": cfg.B,
@@ -222,9 +258,11 @@ def run_workload(args) -> None:
         "cache_resident": per_call * sets < (256 << 20),
         "data": "synthetic", "dtype": "f32",
     }
+    if full is not None:
+        res["roofline"] = full
     if not args.no_cpu:
         import oracle
-        n = min(prob.B, 16 if prob.mode == synth.MODE_DARTREE else 64)
+        n = min(prob.B, {synth.MODE_DART: 64, synth.MODE_DARTREE: 16}.get(prob.mode, 2))
         sample = copy.copy(prob)
         sample.B = n
         sample.logits = prob.logits[:n]

@@ -70,8 +70,13 @@ WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s) {
     w.off_g = take(p->mode == DT_MODE_DARTREE ? rows * k * k * 8 : 0);
     const bool full = p->mode == DT_MODE_DARTREE_FULL;
     const int64_t B = p->B, fw = full ? (int64_t)p->B * p->W : 0, nn = full ? fw * p->d : 0;
-    w.vchunk = kVocabChunk;
-    w.C2 = full ? (int)ceil_div(p->V, kVocabChunk) : 0;
+    // chunks of at least kVocabChunk tokens, about kVocabGroups workgroups
+    // per depth over all request groups
+    const int64_t ngroups = ceil_div(p->B > 0 ? p->B : 1, kVocabReqPerGroup);
+    const int64_t want = kVocabGroups / ngroups > 1 ? kVocabGroups / ngroups : 1;
+    const int64_t vc = round_up(ceil_div(p->V, want), 16);
+    w.vchunk = (int)(vc > kVocabChunk ? vc : kVocabChunk);
+    w.C2 = full ? (int)ceil_div(p->V, w.vchunk) : 0;
     w.off_f_tok = take(fw * 4);
     w.off_f_rk = take(fw * 8);
     w.off_f_s = take(fw * 8);
@@ -83,6 +88,7 @@ WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s) {
     w.off_nd_dep = take(nn * 4);
     w.off_nd_s = take(nn * 8);
     w.off_part = take(fw * w.C2 * (int64_t)sizeof(VocabEntry));
+    w.off_fnorm = take(full ? (int64_t)p->V * 4 : 0);
     w.total = (size_t)round_up(off, 256);
     return w;
 }
@@ -255,6 +261,7 @@ static dt_status build_full(const void* logits, const dt_params* p, const SweepP
     va.logits = logits;
     va.E = p->E;
     va.F = p->F;
+    va.fnorm = (const float*)(ws + w.off_fnorm);
     va.ctx = p->ctx;
     va.f_tok = (const int32_t*)(ws + w.off_f_tok);
     va.f_rk = (const double*)(ws + w.off_f_rk);
@@ -277,6 +284,7 @@ static dt_status build_full(const void* logits, const dt_params* p, const SweepP
     fa.nd_par = (int32_t*)(ws + w.off_nd_par);
     fa.nd_dep = (int32_t*)(ws + w.off_nd_dep);
     fa.nd_s = (double*)(ws + w.off_nd_s);
+    if (launch_fnorm(p->F, p->V, p->R, (float*)(ws + w.off_fnorm), stream) != hipSuccess) return DT_ERR_HIP;
     if (p->prof_event_start && hipEventRecord((hipEvent_t)p->prof_event_start, stream) != hipSuccess)
         return DT_ERR_HIP;
     for (int t = 1; t <= p->d; ++t) {
@@ -335,7 +343,10 @@ extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngr
 
     const SweepPlan s = plan_sweep(p);
     const WorkspacePlan w = plan_workspace(p, s);
-    if (p->mode == DT_MODE_DARTREE_FULL) return build_full(logits, p, s, w, out);
+    if (p->mode == DT_MODE_DARTREE_FULL) {
+        if (w.C2 > kMaxVocabChunks) return DT_ERR_UNSUPPORTED;   // cannot happen: chunks adapt to V
+        return build_full(logits, p, s, w, out);
+    }
     if ((st = launch_sweep_for(logits, p, s, w)) != DT_OK) return st;
 
     char* ws = (char*)p->workspace;

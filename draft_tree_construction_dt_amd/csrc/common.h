@@ -70,10 +70,11 @@ struct SweepPlan {
 //   nd_tok, nd_par, nd_dep    [B][d*W]   candidate-tree nodes in BFS order
 //   nd_s                      [B][d*W]   their cumulative log-scores
 //   part                      [B][C2][W] each vocabulary chunk's top-W (VocabEntry)
+//   fnorm                     [V]        |F_v|, the screen's rounding bound
 struct WorkspacePlan {
     size_t off_m, off_s, off_keys, off_lse, off_ttok, off_tx, off_vmask, off_g;
     size_t off_f_tok, off_f_rk, off_f_s, off_f_node, off_f_n, off_n_tree;
-    size_t off_nd_tok, off_nd_par, off_nd_dep, off_nd_s, off_part;
+    size_t off_nd_tok, off_nd_par, off_nd_dep, off_nd_s, off_part, off_fnorm;
     size_t total;
     int n_ctx_cap;      // contexts per request the vmask area holds (the trigram count)
     int vchunk, C2;     // full-vocabulary mode: columns per chunk and chunk count
@@ -177,8 +178,10 @@ struct NGramUpdateArgs {
 constexpr int kVocabReqPerWave = 2;                       // requests a wave owns
 constexpr int kVocabReqPerGroup = kVocabReqPerWave * kWaves;
 constexpr int kVocabCap = 320;                            // per-(wave, request) candidate buffer
-constexpr int kVocabChunk = 256;                          // vocabulary columns per workgroup
+constexpr int kVocabChunk = 128;                          // least vocabulary columns per workgroup
+constexpr int kVocabGroups = 768;                         // workgroups a depth aims for (three per CU)
 constexpr int kFullMaxW = 16;                             // one 16-row MFMA tile per request
+constexpr int kMaxVocabChunks = 1024;                     // chunks per depth (at most kVocabGroups)
 
 // one entry of a chunk's top-W list: exact key, the parent-conditioned term,
 // the logit and the tie key token * 64 + parent rank (smaller wins)
@@ -196,6 +199,7 @@ struct VocabArgs {
     const void* logits;
     const float* E;
     const float* F;
+    const float* fnorm;            // |F_v| (slightly rounded up), [V]
     const int32_t* ctx;
     const int32_t* f_tok;
     const double* f_rk;
@@ -257,6 +261,7 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_ngram_update(const NGramUpdateArgs& a, hipStream_t stream);
 hipError_t launch_vocab(const VocabArgs& a, hipStream_t stream);
+hipError_t launch_fnorm(const float* F, int V, int R, float* out, hipStream_t stream);
 hipError_t launch_frontier(const FrontierArgs& a, hipStream_t stream);
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
 

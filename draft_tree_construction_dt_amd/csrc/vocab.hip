@@ -39,6 +39,9 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+extern "C" __device__ double __ockl_wfred_max_f64(double);           // DPP wavefront reductions (ROCm ockl)
+extern "C" __device__ unsigned long long __ockl_wfred_min_u64(unsigned long long);
+
 __device__ __forceinline__ unsigned long long ord64(double x) {
     const unsigned long long u = (unsigned long long)__double_as_longlong(x);
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
@@ -47,6 +50,19 @@ __device__ __forceinline__ unsigned long long ord64(double x) {
 __device__ __forceinline__ double unord64(unsigned long long o) {
     const unsigned long long u = (o >> 63) ? (o & 0x7FFFFFFFFFFFFFFFull) : ~o;
     return __longlong_as_double((long long)u);
+}
+
+// raw logit bits (bf16 zero-extended, or fp32), widened only where used, so
+// that a prefetch is not waited for at the load
+template <int DT>
+__device__ __forceinline__ uint32_t load_raw(const void* base, int64_t i) {
+    if (DT == DT_DTYPE_BF16) return (uint32_t)((const uint16_t*)base)[i];
+    return __float_as_uint(((const float*)base)[i]);
+}
+
+template <int DT>
+__device__ __forceinline__ float raw_logit(uint32_t u) {
+    return DT == DT_DTYPE_BF16 ? __uint_as_float(u << 16) : __uint_as_float(u);
 }
 
 template <int DT>
@@ -61,11 +77,7 @@ __device__ __forceinline__ double shfl_d(double v, int src) {
     return __longlong_as_double(((long long)hi << 32) | (uint32_t)lo);
 }
 
-__device__ __forceinline__ double wave_max_d(double v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
-    return v;
-}
+__device__ __forceinline__ double wave_max_d(double v) { return __ockl_wfred_max_f64(v); }
 
 __device__ __forceinline__ int lanes_below(unsigned long long m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -85,18 +97,51 @@ __device__ unsigned long long wave_kth_key(const unsigned long long (&key)[4], i
     return T;
 }
 
-// exact key of one candidate, summed like the oracle: k = 0 .. R-1
-__device__ __forceinline__ double exact_g(const float* __restrict__ E, const float* __restrict__ F, int R,
-                                          int tok, int v) {
+// the kth largest of the wave's 4 x 64 32-bit keys (key 0 = no candidate)
+__device__ uint32_t wave_kth_key32(const uint32_t (&key)[4], int kth) {
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = T | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) n += __popcll(__ballot(key[i] >= c));
+        if (n >= kth) T = c;
+    }
+    return T;
+}
+
+// fp32 screen thresholds of the four output rows a lane holds: a candidate
+// whose fp64 interval reaches lam has (x + acc) + e32 >= thr; the slack
+// covers the fp64 roundings of the key (the screen may only pass more)
+__device__ __forceinline__ void row_thresholds(float (&thr)[4], double lam, const double* rk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        thr[i] = lam == -INFINITY ? -INFINITY
+                                  : __double2float_rd((lam - rk[i]) - 0x1p-40 * (fabs(lam) + fabs(rk[i])));
+}
+
+// exact key of one candidate, summed like the oracle: k = 0 .. R-1 (the rows
+// are loaded in groups of four vectors ahead of the serial sum)
+template <int R>
+__device__ __forceinline__ double exact_g(const float* __restrict__ E, const float* __restrict__ F, int tok, int v) {
     const float4* e4 = reinterpret_cast<const float4*>(E + (int64_t)tok * R);
     const float4* f4 = reinterpret_cast<const float4*>(F + (int64_t)v * R);
     double g = 0.0;
-    for (int q = 0; q < (R >> 2); ++q) {
-        const float4 e = e4[q], f = f4[q];
-        g += (double)e.x * (double)f.x;
-        g += (double)e.y * (double)f.y;
-        g += (double)e.z * (double)f.z;
-        g += (double)e.w * (double)f.w;
+#pragma unroll
+    for (int q0 = 0; q0 < R / 4; q0 += 4) {
+        float4 e[4], f[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            e[u] = e4[q0 + u];
+            f[u] = f4[q0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            g += (double)e[u].x * (double)f[u].x;
+            g += (double)e[u].y * (double)f[u].y;
+            g += (double)e[u].z * (double)f[u].z;
+            g += (double)e[u].w * (double)f[u].w;
+        }
     }
     return g;
 }
@@ -111,37 +156,18 @@ struct VocabLds {
     int tok[kVocabReqPerGroup][16];            // the parents' tokens
 };
 
-// Drop every entry whose interval lies below the W-th largest lower end; the
-// new bound is returned (it never decreases).
-__device__ double compact(VocabLds& L, int slot, int& cnt, double lam, int W, int lane) {
+// Drop every entry whose interval lies below the bound.
+__device__ void compact(VocabLds& L, int slot, int& cnt, double lam, int lane) {
     const int n = cnt;
-    double l_own[kOwn], ak_own[kOwn];
+    double ak_own[kOwn];
     float e_own[kOwn];
     uint32_t id_own[kOwn];
-    double found = -INFINITY;
 #pragma unroll
     for (int r = 0; r < kOwn; ++r) {
         const int q = lane + 64 * r;
         ak_own[r] = q < n ? L.ak[slot][q] : -INFINITY;
         e_own[r] = q < n ? L.e[slot][q] : 0.f;
         id_own[r] = q < n ? L.id[slot][q] : 0u;
-        l_own[r] = ak_own[r] - (double)e_own[r];
-    }
-    if (n >= W) {
-#pragma unroll
-        for (int r = 0; r < kOwn; ++r) {
-            const int q = lane + 64 * r;
-            int rank = 0;
-            if (q < n) {
-                for (int j = 0; j < n; ++j) {
-                    const double lj = L.ak[slot][j] - (double)L.e[slot][j];
-                    rank += (lj > l_own[r]) | ((lj == l_own[r]) & (j < q));
-                }
-                if (rank == W - 1) found = l_own[r];
-            }
-        }
-        found = wave_max_d(found);
-        lam = fmax(lam, found);
     }
     __builtin_amdgcn_wave_barrier();
     int base = 0;
@@ -160,12 +186,30 @@ __device__ double compact(VocabLds& L, int slot, int& cnt, double lam, int W, in
     }
     __builtin_amdgcn_wave_barrier();
     cnt = base;
-    return lam;
+}
+
+// The W largest lower ends inserted so far, descending, in lanes 0..W-1
+// (-inf where fewer); the bound is the W-th.
+__device__ __forceinline__ void top_insert(double& lst, double y, int W, int lane) {
+    const int pos = __popcll(__ballot(lane < W && lst >= y));
+    if (pos >= W) return;                                               // wave-uniform
+    const long long u = __double_as_longlong(lst);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(u & 0xFFFFFFFFll), 0x111, 0xF, 0xF, false);  // row_shr:1
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), 0x111, 0xF, 0xF, false);
+    const double up = __longlong_as_double(((long long)hi << 32) | (uint32_t)lo);
+    lst = lane < pos ? lst : (lane == pos ? y : up);
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const long long u = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(u & 0xFFFFFFFFll), l);
+    const int hi = __builtin_amdgcn_readlane((int)(u >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (uint32_t)lo);
 }
 
 // Rescore every entry exactly and keep the exact top-W, sorted.  With `out`
 // set, the list is also written there (W entries, empties padded).
-template <int DT>
+template <int DT, int R>
 __device__ double finalize(VocabLds& L, int slot, int& cnt, int W, int lane, const VocabArgs& a, int b,
                            VocabEntry* out) {
     const int n = cnt;
@@ -185,7 +229,7 @@ __device__ double finalize(VocabLds& L, int slot, int& cnt, int W, int lane, con
             const int v = (int)(id >> 4), p = (int)(id & 15u);
             const float x = load_logit<DT>(a.logits, row + v);
             const int ptok = L.tok[slot][p];
-            const double g = ptok >= 0 ? exact_g(a.E, a.F, a.R, ptok, v) : 0.0;
+            const double g = ptok >= 0 ? exact_g<R>(a.E, a.F, ptok, v) : 0.0;
             K[r] = (L.rk[slot][p] + (double)x) + g;
             G[r] = g;
             X[r] = x;
@@ -250,7 +294,7 @@ __device__ double finalize(VocabLds& L, int slot, int& cnt, int W, int lane, con
 }
 
 template <int DT, int KS>
-__global__ void __launch_bounds__(kThreads) vocab_kernel(VocabArgs a) {
+__global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
     __shared__ VocabLds L;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -264,7 +308,6 @@ __global__ void __launch_bounds__(kThreads) vocab_kernel(VocabArgs a) {
 
     // ---- the frontier rows of the wave's requests: A operands, Rk, |E_p|
     float A[kVocabReqPerWave][KS];
-    double rk[kVocabReqPerWave][4];
     float eb[kVocabReqPerWave][4];
     int nf[kVocabReqPerWave], bq[kVocabReqPerWave];
 #pragma unroll
@@ -305,90 +348,155 @@ __global__ void __launch_bounds__(kThreads) vocab_kernel(VocabArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * kq + i;
             eb[j][i] = 0x1p-17f * sqrtf(__shfl(ne, r));
-            rk[j][i] = shfl_d(rkm, r);
         }
     }
     __builtin_amdgcn_wave_barrier();
 
-    double lam[kVocabReqPerWave];
+    double lam[kVocabReqPerWave], lst[kVocabReqPerWave];
     int cnt[kVocabReqPerWave];
+    float thr[kVocabReqPerWave][4];
 #pragma unroll
     for (int j = 0; j < kVocabReqPerWave; ++j) {
         lam[j] = -INFINITY;
+        lst[j] = -INFINITY;
         cnt[j] = 0;
+        row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq]);
     }
     const int64_t rowoff = (int64_t)(a.t - 1) * a.V;
+    int64_t xrow[kVocabReqPerWave];
+#pragma unroll
+    for (int j = 0; j < kVocabReqPerWave; ++j) xrow[j] = nf[j] > 0 ? (int64_t)bq[j] * a.d * a.V + rowoff : 0;
     const int nblk = (ncol + 15) >> 4;
-    for (int cb = 0; cb < nblk; ++cb) {
-        const int cl = cb * 16 + m;
-        const bool vv = cl < ncol;
-        const int v = col0 + (vv ? cl : 0);
-        float f[KS];
+
+    // block cb + 1's F rows, norms and logits are loaded while block cb is
+    // scored; every load reads a valid address (the last column for the
+    // padding of a ragged chunk) and validity is applied where the block is
+    // used
+    float fc[KS], nc;
+    uint32_t xc[kVocabReqPerWave];
+    {
+        const int v = col0 + (m < ncol ? m : ncol - 1);
+        nc = a.fnorm[v];
         const float4* fr = reinterpret_cast<const float4*>(a.F + (int64_t)v * R + kq * KS);
 #pragma unroll
         for (int s4 = 0; s4 < KS / 4; ++s4) {
-            const float4 q = vv ? fr[s4] : make_float4(0.f, 0.f, 0.f, 0.f);
-            f[4 * s4 + 0] = q.x;
-            f[4 * s4 + 1] = q.y;
-            f[4 * s4 + 2] = q.z;
-            f[4 * s4 + 3] = q.w;
+            const float4 q = fr[s4];
+            fc[4 * s4 + 0] = q.x;
+            fc[4 * s4 + 1] = q.y;
+            fc[4 * s4 + 2] = q.z;
+            fc[4 * s4 + 3] = q.w;
         }
-        float nfv = 0.f;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) nfv += f[s] * f[s];
-        nfv += __shfl_xor(nfv, 16);
-        nfv += __shfl_xor(nfv, 32);
-        nfv = sqrtf(nfv);
+        for (int j = 0; j < kVocabReqPerWave; ++j) xc[j] = load_raw<DT>(a.logits, xrow[j] + v);
+    }
+    for (int cb = 0; cb < nblk; ++cb) {
+        const int cl = cb * 16 + m;
+        const bool vv = cl < ncol;
+        const int v = col0 + (vv ? cl : ncol - 1);
+        float fn[KS], nn = 0.f;
+        uint32_t xn[kVocabReqPerWave];
+        if (cb + 1 < nblk) {                                            // wave-uniform
+            const int cln = cl + 16;
+            const int vn = col0 + (cln < ncol ? cln : ncol - 1);
+            nn = a.fnorm[vn];
+            const float4* fr = reinterpret_cast<const float4*>(a.F + (int64_t)vn * R + kq * KS);
+#pragma unroll
+            for (int s4 = 0; s4 < KS / 4; ++s4) {
+                const float4 q = fr[s4];
+                fn[4 * s4 + 0] = q.x;
+                fn[4 * s4 + 1] = q.y;
+                fn[4 * s4 + 2] = q.z;
+                fn[4 * s4 + 3] = q.w;
+            }
+#pragma unroll
+            for (int j = 0; j < kVocabReqPerWave; ++j) xn[j] = load_raw<DT>(a.logits, xrow[j] + vn);
+        }
+        const float nfv = nc;
+        v4f acc[kVocabReqPerWave];
+#pragma unroll
+        for (int j = 0; j < kVocabReqPerWave; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int j = 0; j < kVocabReqPerWave; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[j][s], fc[s], acc[j], 0, 0, 0);
+        }
 #pragma unroll
         for (int j = 0; j < kVocabReqPerWave; ++j) {
             if (nf[j] == 0) continue;                                   // wave-uniform
             const int slot = wave * kVocabReqPerWave + j;
-            const float x = vv ? load_logit<DT>(a.logits, (int64_t)bq[j] * a.d * a.V + rowoff + v) : -INFINITY;
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[j][s], f[s], acc, 0, 0, 0);
-            double ak[4];
-            float e[4];
-            bool ok[4];
+            const float x = vv ? raw_logit<DT>(xc[j]) : -INFINITY;
+            bool ok[4], pf[4];
+            bool anyp = false;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 ok[i] = (4 * kq + i < nf[j]) && x != -INFINITY;
-                ak[i] = (rk[j][i] + (double)x) + (double)acc[i];
-                e[i] = eb[j][i] * nfv + fabsf((float)ak[i]) * 0x1p-44f + 0x1p-100f;
+                const float sx = x + acc[j][i];
+                const float e32 = fmaf(eb[j][i], nfv, fabsf(sx) * 0x1p-22f + 0x1p-100f);
+                pf[i] = ok[i] && sx + e32 >= thr[j][i];
+                anyp |= pf[i];
             }
             if (lam[j] == -INFINITY) {
-                // seed the bound with the W-th largest lower end of this tile
-                unsigned long long key[4];
+                // seed the bound: the W-th largest lower end of this tile,
+                // rounded down to fp32
+                uint32_t key[4];
                 int nv = 0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    key[i] = ok[i] ? ord64(ak[i] - (double)e[i]) : 0ull;
+                    const double ak = (L.rk[slot][4 * kq + i] + (double)x) + (double)acc[j][i];
+                    const float e = eb[j][i] * nfv + fabsf((float)ak) * 0x1p-44f + 0x1p-100f;
+                    key[i] = ok[i] ? ord_bits(__float_as_uint(__double2float_rd(ak - (double)e))) : 0u;
                     nv += __popcll(__ballot(ok[i]));
                 }
-                if (nv >= W) lam[j] = unord64(wave_kth_key(key, W));
+                if (nv >= W) {
+                    lam[j] = (double)__uint_as_float(unord_bits(wave_kth_key32(key, W)));
+                    row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq]);
+                }
             }
+            if (__ballot(anyp) == 0) continue;                          // nothing reaches the bound
             int base = cnt[j];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool pass = ok[i] && ak[i] + (double)e[i] >= lam[j];
-                const unsigned long long bm = __ballot(pass);
+                const double ak = (L.rk[slot][4 * kq + i] + (double)x) + (double)acc[j][i];
+                const float e = eb[j][i] * nfv + fabsf((float)ak) * 0x1p-44f + 0x1p-100f;
+                const bool pass = pf[i] && ak + (double)e >= lam[j];
+                unsigned long long bm = __ballot(pass);
                 if (pass) {
                     const int pos = base + lanes_below(bm);
-                    L.ak[slot][pos] = ak[i];
-                    L.e[slot][pos] = e[i];
+                    L.ak[slot][pos] = ak;
+                    L.e[slot][pos] = e;
                     L.id[slot][pos] = ((uint32_t)v << 4) | (uint32_t)(4 * kq + i);
                 }
                 base += __popcll(bm);
+                // the bound follows the W-th largest lower end inserted
+                const double lo = ak - (double)e;
+                while (bm) {
+                    const int src = __builtin_ctzll(bm);
+                    bm &= bm - 1;
+                    top_insert(lst[j], readlane_d(lo, src), W, lane);
+                }
             }
             __builtin_amdgcn_wave_barrier();
             cnt[j] = base;
+            const double lw = readlane_d(lst[j], W - 1);
+            if (lw > lam[j]) lam[j] = lw;
             if (cnt[j] > kVocabCap - 256) {
-                // room for the next tile: tighten, and if intervals still
-                // overlap too much (ties), settle the order exactly
-                lam[j] = compact(L, slot, cnt[j], lam[j], W, lane);
-                if (cnt[j] > kVocabCap - 256)
-                    lam[j] = finalize<DT>(L, slot, cnt[j], W, lane, a, bq[j], nullptr);
+                // room for the next tile; if intervals still overlap too much
+                // (ties), settle the order exactly
+                compact(L, slot, cnt[j], lam[j], lane);
+                if (cnt[j] > kVocabCap - 256) {
+                    lam[j] = fmax(lam[j], finalize<DT, R>(L, slot, cnt[j], W, lane, a, bq[j], nullptr));
+                    lst[j] = lane < cnt[j] ? L.ak[slot][lane < kVocabCap ? lane : 0] : -INFINITY;
+                }
             }
+            row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq]);
+        }
+        if (cb + 1 < nblk) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) fc[s] = fn[s];
+#pragma unroll
+            for (int j = 0; j < kVocabReqPerWave; ++j) xc[j] = xn[j];
+            nc = nn;
         }
     }
 
@@ -399,8 +507,8 @@ __global__ void __launch_bounds__(kThreads) vocab_kernel(VocabArgs a) {
         if (b >= a.B) continue;                                         // wave-uniform
         const int slot = wave * kVocabReqPerWave + j;
         VocabEntry* out = a.part + ((int64_t)b * a.C2 + c) * W;
-        if (cnt[j] > W) lam[j] = compact(L, slot, cnt[j], lam[j], W, lane);
-        finalize<DT>(L, slot, cnt[j], W, lane, a, b, out);
+        if (cnt[j] > W) compact(L, slot, cnt[j], lam[j], lane);
+        finalize<DT, R>(L, slot, cnt[j], W, lane, a, b, out);
     }
 }
 
@@ -408,79 +516,124 @@ __global__ void __launch_bounds__(kThreads) vocab_kernel(VocabArgs a) {
 // frontier merge: one workgroup per request
 // ---------------------------------------------------------------------------
 constexpr int kFrontCap = 1024;
+constexpr int kHeadsPerLane = kMaxVocabChunks / 64;
 
 __device__ __forceinline__ bool entry_before(double ka, uint32_t ta, double kb, uint32_t tb) {
     return ka > kb || (ka == kb && ta < tb);
 }
 
-__global__ void __launch_bounds__(kThreads) frontier_kernel(FrontierArgs a) {
+// One wave per request.  The chunk lists are sorted, so the W-th largest of
+// their heads bounds the frontier's W-th key from below (W distinct entries
+// reach it) and only entries at or above it can be selected; they are ranked
+// exactly by (Rk desc, tie asc).
+__global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
     __shared__ double s_k[kFrontCap];
     __shared__ uint32_t s_t[kFrontCap];
     __shared__ int s_src[kFrontCap];
-    __shared__ double s_red_k[kWaves];
-    __shared__ uint32_t s_red_t[kWaves];
-    __shared__ int s_cnt;
     __shared__ int s_win[kFullMaxW];
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.x, lane = threadIdx.x;
     const int W = a.W, C2 = a.C2;
     const VocabEntry* lists = a.part + (int64_t)b * C2 * W;
 
-    // 1. a lower bound for the frontier's W-th key: the best W-th entry of any list
-    double hk = -INFINITY;
-    uint32_t ht = 0xFFFFFFFFu;
-    for (int c = tid; c < C2; c += kThreads) {
-        const VocabEntry& e = lists[(int64_t)c * W + (W - 1)];
-        if (e.rk != -INFINITY && entry_before(e.rk, e.tie, hk, ht)) {
-            hk = e.rk;
-            ht = e.tie;
-        }
-    }
+    // 1. the heads, then the W-th largest of them by W extractions
+    double hk[kHeadsPerLane];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const double ok = __shfl_xor(hk, off);
-        const uint32_t ot = __shfl_xor(ht, off);
-        if (entry_before(ok, ot, hk, ht)) {
-            hk = ok;
-            ht = ot;
-        }
+    for (int q = 0; q < kHeadsPerLane; ++q) {
+        const int c = lane + 64 * q;
+        hk[q] = c < C2 ? lists[(int64_t)c * W].rk : -INFINITY;
     }
-    if (lane == 0) {
-        s_red_k[wave] = hk;
-        s_red_t[wave] = ht;
+    uint32_t taken = 0;
+    double bound = -INFINITY;
+    int found = 0;
+    for (int r = 0; r < W; ++r) {
+        double lb = -INFINITY;
+        int lq = -1;
+#pragma unroll
+        for (int q = 0; q < kHeadsPerLane; ++q)
+            if (!((taken >> q) & 1u) && hk[q] != -INFINITY && (lq < 0 || hk[q] > lb)) {
+                lb = hk[q];
+                lq = q;
+            }
+        const double wb = wave_max_d(lq >= 0 ? lb : -INFINITY);
+        if (wb == -INFINITY) break;                                   // fewer than W heads
+        const int wl = __builtin_ctzll(__ballot(lq >= 0 && lb == wb));
+        if (lane == wl) taken |= 1u << lq;
+        bound = wb;
+        ++found;
     }
-    if (tid == 0) s_cnt = 0;
+    if (found < W) bound = -INFINITY;
     __syncthreads();
-    hk = s_red_k[0];
-    ht = s_red_t[0];
-    for (int w = 1; w < kWaves; ++w)
-        if (entry_before(s_red_k[w], s_red_t[w], hk, ht)) {
-            hk = s_red_k[w];
-            ht = s_red_t[w];
-        }
 
-    // 2. every entry at or above the bound (lists are sorted)
-    for (int c = tid; c < C2; c += kThreads) {
-        for (int r = 0; r < W; ++r) {
-            const int64_t idx = (int64_t)c * W + r;
-            const VocabEntry& e = lists[idx];
-            if (e.rk == -INFINITY) break;
-            if (hk != -INFINITY && entry_before(hk, ht, e.rk, e.tie)) break;
-            const int pos = atomicAdd(&s_cnt, 1);
+    // 2. every entry at or above the bound: the qualifying lists (head at or
+    //    above it) are read 64 entries per round, all lanes loading at once
+    __shared__ int s_q[kMaxVocabChunks];
+    int nq = 0;
+#pragma unroll
+    for (int q = 0; q < kHeadsPerLane; ++q) {
+        const int c = lane + 64 * q;
+        const bool qual = c < C2 && hk[q] != -INFINITY && hk[q] >= bound;
+        const unsigned long long m = __ballot(qual);
+        if (qual) s_q[nq + lanes_below(m)] = c;
+        nq += __popcll(m);
+    }
+    __syncthreads();
+    int n = 0;
+    const int items = nq * W;
+    for (int it0 = 0; it0 < items; it0 += 64) {
+        const int it = it0 + lane;
+        double k = -INFINITY;
+        uint32_t t = 0xFFFFFFFFu;
+        int idx = 0;
+        if (it < items) {
+            const int qi = it / W, r = it - qi * W;
+            idx = s_q[qi] * W + r;
+            k = lists[idx].rk;
+            t = lists[idx].tie;
+        }
+        const bool take = k != -INFINITY && k >= bound;
+        const unsigned long long m = __ballot(take);
+        if (take) {
+            const int pos = n + lanes_below(m);
             if (pos < kFrontCap) {
-                s_k[pos] = e.rk;
-                s_t[pos] = e.tie;
-                s_src[pos] = (int)idx;
+                s_k[pos] = k;
+                s_t[pos] = t;
+                s_src[pos] = idx;
             }
         }
+        n += __popcll(m);
     }
     __syncthreads();
-    const int n = s_cnt;
     const int nsel = n < W ? n : W;
     if (n <= kFrontCap) {
-        for (int q = tid; q < n; q += kThreads) {
-            int r = 0;
-            for (int j = 0; j < n; ++j) r += entry_before(s_k[j], s_t[j], s_k[q], s_t[q]);
-            if (r < W) s_win[r] = s_src[q];
+        // W extractions over the candidates, 16 per lane in registers
+        double ck[kFrontCap / 64];
+        uint32_t ct[kFrontCap / 64];
+#pragma unroll
+        for (int q = 0; q < kFrontCap / 64; ++q) {
+            const int pos = lane + 64 * q;
+            ck[q] = pos < n ? s_k[pos] : -INFINITY;
+            ct[q] = pos < n ? s_t[pos] : 0xFFFFFFFFu;
+        }
+        uint32_t used = 0;
+        for (int r = 0; r < nsel; ++r) {
+            double bk = -INFINITY;
+            uint32_t bt = 0xFFFFFFFFu;
+            int bq = -1;
+#pragma unroll
+            for (int q = 0; q < kFrontCap / 64; ++q)
+                if (lane + 64 * q < n && !((used >> q) & 1u) && (bq < 0 || entry_before(ck[q], ct[q], bk, bt))) {
+                    bk = ck[q];
+                    bt = ct[q];
+                    bq = q;
+                }
+            const double mk = wave_max_d(bq >= 0 ? bk : -INFINITY);
+            const bool atk = bq >= 0 && bk == mk;
+            const unsigned long long mt = __ockl_wfred_min_u64(atk ? (unsigned long long)bt : ~0ull);
+            const int bl = __builtin_ctzll(__ballot(atk && (unsigned long long)bt == mt));
+            if (lane == bl) {
+                used |= 1u << bq;
+                s_win[r] = s_src[lane + 64 * bq];
+            }
         }
     } else {
         // many exact ties at the bound: take the best W one at a time
@@ -490,12 +643,13 @@ __global__ void __launch_bounds__(kThreads) frontier_kernel(FrontierArgs a) {
             double bk = -INFINITY;
             uint32_t bt = 0xFFFFFFFFu;
             int bi = -1;
-            for (int64_t idx = tid; idx < (int64_t)C2 * W; idx += kThreads) {
-                const VocabEntry& e = lists[idx];
-                if (e.rk == -INFINITY || !entry_before(pk, pt, e.rk, e.tie)) continue;
-                if (bi < 0 || entry_before(e.rk, e.tie, bk, bt)) {
-                    bk = e.rk;
-                    bt = e.tie;
+            for (int64_t idx = lane; idx < (int64_t)C2 * W; idx += 64) {
+                const double k = lists[idx].rk;
+                const uint32_t t = lists[idx].tie;
+                if (k == -INFINITY || !entry_before(pk, pt, k, t)) continue;
+                if (bi < 0 || entry_before(k, t, bk, bt)) {
+                    bk = k;
+                    bt = t;
                     bi = (int)idx;
                 }
             }
@@ -510,23 +664,7 @@ __global__ void __launch_bounds__(kThreads) frontier_kernel(FrontierArgs a) {
                     bi = oi;
                 }
             }
-            __syncthreads();
-            if (lane == 0) {
-                s_red_k[wave] = bk;
-                s_red_t[wave] = bt;
-                s_src[wave] = bi;
-            }
-            __syncthreads();
-            bk = -INFINITY;
-            bt = 0xFFFFFFFFu;
-            bi = -1;
-            for (int w = 0; w < kWaves; ++w)
-                if (s_src[w] >= 0 && (bi < 0 || entry_before(s_red_k[w], s_red_t[w], bk, bt))) {
-                    bk = s_red_k[w];
-                    bt = s_red_t[w];
-                    bi = s_src[w];
-                }
-            if (tid == 0) s_win[r] = bi;
+            if (lane == 0) s_win[r] = bi;
             pk = bk;
             pt = bt;
         }
@@ -537,36 +675,60 @@ __global__ void __launch_bounds__(kThreads) frontier_kernel(FrontierArgs a) {
     const int base = a.t == 1 ? 0 : a.n_tree[b];
     const int64_t fb = (int64_t)b * W;
     int tok = 0, pnode = -1;
-    double rkv = 0.0, s = 0.0;
-    if (tid < nsel) {
-        const VocabEntry& e = lists[s_win[tid]];
+    double rkv = 0.0, sc = 0.0;
+    if (lane < nsel) {
+        const VocabEntry& e = lists[s_win[lane]];
         tok = (int)(e.tie >> 6);
         const int pr = (int)(e.tie & 63u);
         const double ps = a.t == 1 ? 0.0 : a.f_s[fb + pr];
         pnode = a.t == 1 ? -1 : a.f_node[fb + pr];
         rkv = e.rk;
-        s = (ps + ((double)e.x - a.lse[(int64_t)b * a.d + (a.t - 1)])) + e.g;
+        sc = (ps + ((double)e.x - a.lse[(int64_t)b * a.d + (a.t - 1)])) + e.g;
     }
     __syncthreads();
-    if (tid < nsel) {
-        const int node = base + tid;
+    if (lane < nsel) {
+        const int node = base + lane;
         const int64_t nb = (int64_t)b * a.d * W + node;
         a.nd_tok[nb] = tok;
         a.nd_par[nb] = pnode;
         a.nd_dep[nb] = a.t;
-        a.nd_s[nb] = s;
-        a.f_tok[fb + tid] = tok;
-        a.f_rk[fb + tid] = rkv;
-        a.f_s[fb + tid] = s;
-        a.f_node[fb + tid] = node;
+        a.nd_s[nb] = sc;
+        a.f_tok[fb + lane] = tok;
+        a.f_rk[fb + lane] = rkv;
+        a.f_s[fb + lane] = sc;
+        a.f_node[fb + lane] = node;
     }
-    if (tid == 0) {
+    if (lane == 0) {
         a.f_n[b] = nsel;
         a.n_tree[b] = base + nsel;
     }
 }
 
+// |F_v| for every token, once per call (the rounding bound of the screen)
+template <int R>
+__global__ void __launch_bounds__(kThreads) fnorm_kernel(const float* __restrict__ F, int V, float* __restrict__ out) {
+    const int v = blockIdx.x * kThreads + threadIdx.x;
+    if (v >= V) return;
+    const float4* f4 = reinterpret_cast<const float4*>(F + (int64_t)v * R);
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q) {
+        const float4 f = f4[q];
+        s += f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
+    }
+    out[v] = sqrtf(s) * (1.f + 0x1p-20f);
+}
+
 }  // namespace
+
+hipError_t launch_fnorm(const float* F, int V, int R, float* out, hipStream_t stream) {
+    const dim3 grid((unsigned)((V + kThreads - 1) / kThreads)), block(kThreads);
+    if (R == 16) hipLaunchKernelGGL(fnorm_kernel<16>, grid, block, 0, stream, F, V, out);
+    else if (R == 32) hipLaunchKernelGGL(fnorm_kernel<32>, grid, block, 0, stream, F, V, out);
+    else if (R == 64) hipLaunchKernelGGL(fnorm_kernel<64>, grid, block, 0, stream, F, V, out);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_vocab(const VocabArgs& a, hipStream_t stream) {
     if (a.B <= 0) return hipSuccess;
@@ -594,7 +756,7 @@ hipError_t launch_vocab(const VocabArgs& a, hipStream_t stream) {
 
 hipError_t launch_frontier(const FrontierArgs& a, hipStream_t stream) {
     if (a.B <= 0) return hipSuccess;
-    hipLaunchKernelGGL(frontier_kernel, dim3((unsigned)a.B), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(frontier_kernel, dim3((unsigned)a.B), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
