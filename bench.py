@@ -433,6 +433,33 @@ def main():
     b1_wall, _ = run(1, list(range(nreq)), K1, min(200, K1), nstream)
     b1_one, _ = run(1, list(range(nreq)), K1, min(200, K1), 1)
 
+    # ---- B = 1 replayed from HIP graphs: one captured call per request,
+    #      replayed round-robin back to back (the library enqueues kernels
+    #      only, so the whole call is capturable)
+    ng_graphs = min(64, nreq)
+    out_g = bd.alloc_tree_out(1, prob.budget, dev)
+    og = out_g._c()
+    keep_g, graphs = [], []
+    for r in range(ng_graphs):
+        q = params(1, r, None)
+        keep_g.append(q)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            qc = q._c()
+            st = fn(logits[r].data_ptr(), ctypes.byref(ng_c), ctypes.byref(qc), ctypes.byref(og))
+            if st != 0:
+                raise bd.DtError(st, "dt_build_tree (capture)")
+        graphs.append(gr)
+    for gr in graphs:
+        gr.replay()
+    torch.cuda.synchronize()
+    tg = time.perf_counter()
+    for i in range(K1):
+        graphs[i % ng_graphs].replay()
+    torch.cuda.synchronize()
+    b1_graph = time.perf_counter() - tg
+    del graphs
+
     upd = time_ngram_update(lib, ngram, prob, dev, args.update_steps, 100, args.seed)
 
     achieved = logit_bytes / sweep_avg_s / 1e9
@@ -470,6 +497,9 @@ def main():
             "us_per_tree": b1_one / K1 * 1e6,
             "trees_per_s": K1 / b1_one,
             "timing": "one stream, calls back to back: the latency of one request",
+            "graph_us_per_tree": b1_graph / K1 * 1e6,
+            "graph_timing": f"the same calls captured in {ng_graphs} HIP graphs (one per request) and replayed "
+                            "round-robin back to back on one stream",
             "trees_per_s_streams": K1 / b1_wall,
             "streams": nstream,
             "steps": K1,
