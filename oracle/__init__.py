@@ -78,6 +78,10 @@ def _load():
         lib.oracle_ngram_update.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+        lib.oracle_verify_length.restype = ctypes.c_int
+        lib.oracle_verify_length.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                             ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_build_tree.restype = ctypes.c_int
         lib.oracle_build_tree.argtypes = [
             ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
@@ -203,3 +207,22 @@ def ngram_update(ngram, ctx, tokens, lengths, new_logp: float = 0.0):
     if rc != 0:
         raise ValueError("oracle_ngram_update: invalid arguments")
     return tuple(int(x) for x in counts)
+
+
+def verify_length(tree: dict, cost_fixed: float, cost_per_token: float):
+    """How many best-first nodes of each tree to verify, and every node's
+    best-first position (see oracle_verify_length).  ``tree`` holds the
+    arrays build_tree returns.  Returns (n_verify int32[B], rank int32[B][budget])."""
+    n_nodes = np.ascontiguousarray(tree["n_nodes"], dtype=np.int32)
+    parents = np.ascontiguousarray(tree["parents"], dtype=np.int32)
+    depths = np.ascontiguousarray(tree["depths"], dtype=np.int32)
+    scores = np.ascontiguousarray(tree["scores"], dtype=np.float32)
+    B, budget = parents.shape
+    n_verify = np.zeros(B, dtype=np.int32)
+    rank = np.zeros((B, budget), dtype=np.int32)
+    rc = _load().oracle_verify_length(n_nodes.ctypes.data, parents.ctypes.data, depths.ctypes.data,
+                                      scores.ctypes.data, int(B), int(budget), float(cost_fixed),
+                                      float(cost_per_token), n_verify.ctypes.data, rank.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_verify_length: invalid arguments")
+    return n_verify, rank

@@ -384,3 +384,47 @@ int oracle_ngram_update(uint64_t* keys, int32_t* succ, float* hash_logp, int64_t
     }
     return 0;
 }
+
+/* ---- how many nodes to verify ------------------------------------------- */
+
+int oracle_verify_length(const int32_t* n_nodes, const int32_t* parents, const int32_t* depths,
+                         const float* scores, int B, int budget, double cost_fixed, double cost_per_token,
+                         int32_t* n_verify, int32_t* rank) {
+    if (B < 0 || budget < 1 || !(cost_fixed > 0.0) || !(cost_per_token >= 0.0)) return -1;
+    char* taken = (char*)malloc((size_t)budget);
+    int32_t* order = (int32_t*)malloc((size_t)budget * sizeof(int32_t));
+    for (int b = 0; b < B; ++b) {
+        const int n = n_nodes[b];
+        const int32_t* par = parents + (size_t)b * budget;
+        const int32_t* dep = depths + (size_t)b * budget;
+        const float* sc = scores + (size_t)b * budget;
+        int32_t* rk = rank + (size_t)b * budget;
+        for (int i = 0; i < budget; ++i) rk[i] = -1;
+        memset(taken, 0, (size_t)budget);
+        /* best-first order over the tree */
+        for (int step = 0; step < n; ++step) {
+            int best = -1;
+            for (int i = 0; i < n; ++i) {
+                if (taken[i] || (par[i] >= 0 && !taken[par[i]])) continue;
+                if (best < 0 || sc[i] > sc[best] || (sc[i] == sc[best] && dep[i] < dep[best])) best = i;
+            }
+            taken[best] = 1;
+            rk[best] = step;
+            order[step] = best;
+        }
+        /* extend while the expected tokens per unit cost strictly grow */
+        double A = 1.0, T = cost_fixed;
+        int m = 0;
+        while (m < n) {
+            const double c = exp((double)sc[order[m]]);
+            if (!(c * T > cost_per_token * A)) break;
+            A += c;
+            T += cost_per_token;
+            ++m;
+        }
+        n_verify[b] = m;
+    }
+    free(taken);
+    free(order);
+    return 0;
+}

@@ -112,6 +112,24 @@ int oracle_ngram_update(uint64_t* keys, int32_t* succ, float* hash_logp, int64_t
                         const int32_t* ctx, const int32_t* tokens, const int32_t* lengths,
                         int B, int L, float new_logp, int64_t* counts);
 
+/* How many nodes of a built tree to verify (LibraSpec, scholarbro listing
+ * abstract: the speculative length is chosen by expected speedup, extending
+ * only while the acceptance gain outweighs the extra verification cost,
+ * judged from the drafter's confidence).  For each request, in best-first
+ * order over its tree (a node is available once its parent is taken; the
+ * best available by (score desc, depth asc, index asc) is taken next), node
+ * n has confidence c_n = exp(score_n), the drafter's probability that its
+ * whole path is accepted.  With A(n) = 1 + sum_{i<n} c_i expected tokens per
+ * round and T(n) = cost_fixed + cost_per_token * n the round's cost, node n
+ * is added while c_n * T(n) > cost_per_token * A(n), i.e. while A/T strictly
+ * grows; the first n where it does not is n_verify.  rank[b][i] receives the
+ * best-first position of node i (-1 for rows past n_nodes).  Inputs are the
+ * tree arrays as dt_build_tree writes them (host memory here).  Returns 0,
+ * or -1 on invalid arguments (cost_fixed <= 0, cost_per_token < 0). */
+int oracle_verify_length(const int32_t* n_nodes, const int32_t* parents, const int32_t* depths,
+                         const float* scores, int B, int budget, double cost_fixed, double cost_per_token,
+                         int32_t* n_verify, int32_t* rank);
+
 #ifdef __cplusplus
 }
 #endif
