@@ -460,6 +460,31 @@ def main():
     b1_graph = time.perf_counter() - tg
     del graphs
 
+    # ---- how many of each B=64 tree's nodes to verify (expected-speedup rule)
+    qv = params(BATCH, 0, None)
+    out_v = bd.alloc_tree_out(BATCH, prob.budget, dev)
+    ov = out_v._c()
+    qvc = qv._c()
+    if fn(logits[0].data_ptr(), ctypes.byref(ng_c), ctypes.byref(qvc), ctypes.byref(ov)) != 0:
+        raise RuntimeError("dt_build_tree")
+    nv = torch.empty(BATCH, dtype=torch.int32, device=dev)
+    rank = torch.empty(BATCH, prob.budget, dtype=torch.int32, device=dev)
+    vfn = lib.dt_verify_length
+    hv = torch.cuda.current_stream().cuda_stream
+    cost_fixed, cost_per_token = 16.0, 1.0
+    for _ in range(20):
+        vfn(ctypes.byref(ov), BATCH, prob.budget, cost_fixed, cost_per_token, ctypes.c_void_p(nv.data_ptr()),
+            ctypes.c_void_p(rank.data_ptr()), hv)
+    torch.cuda.synchronize()
+    tv = time.perf_counter()
+    KV = 1000
+    for _ in range(KV):
+        vfn(ctypes.byref(ov), BATCH, prob.budget, cost_fixed, cost_per_token, ctypes.c_void_p(nv.data_ptr()),
+            ctypes.c_void_p(rank.data_ptr()), hv)
+    torch.cuda.synchronize()
+    verify_us = (time.perf_counter() - tv) / KV * 1e6
+    nv_host = nv.cpu().numpy()
+
     upd = time_ngram_update(lib, ngram, prob, dev, args.update_steps, 100, args.seed)
 
     achieved = logit_bytes / sweep_avg_s / 1e9
@@ -505,6 +530,13 @@ def main():
             "steps": K1,
         },
         "ngram_update": upd,
+        "verify_length": {
+            "workload": f"the {BATCH} trees of input set 0, cost_fixed={cost_fixed}, cost_per_token={cost_per_token} "
+                        "(a round's fixed cost as 16 verified tokens)",
+            "us_per_call": verify_us,
+            "n_verify_mean": float(nv_host.mean()),
+            "timing": "wall clock of back-to-back calls on one stream",
+        },
         "roofline": {
             "bound": "hbm",
             "kernel": "sweep_kernel<bf16>",

@@ -67,7 +67,8 @@ class _TreeOut(ctypes.Structure):
                 ("scores", ctypes.c_void_p), ("mask", ctypes.c_void_p)]
 
 
-EXPORTED = ("dt_build_tree", "dt_workspace_size", "dt_status_string", "dt_position_topk", "dt_ngram_update")
+EXPORTED = ("dt_build_tree", "dt_workspace_size", "dt_status_string", "dt_position_topk", "dt_ngram_update",
+            "dt_verify_length")
 
 _lib = None
 
@@ -97,6 +98,9 @@ def _load():
         lib.dt_ngram_update.argtypes = [ctypes.POINTER(_NGram), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
                                         ctypes.c_void_p]
+        lib.dt_verify_length.restype = ctypes.c_int
+        lib.dt_verify_length.argtypes = [ctypes.POINTER(_TreeOut), ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                         ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -232,6 +236,24 @@ def dt_ngram_update(ngram: "NGram", ctx: torch.Tensor, tokens: torch.Tensor, len
                                  float(new_logp), _ptr(counts), h)
     if st != DT_OK:
         raise DtError(st, "dt_ngram_update")
+
+
+def dt_verify_length(tree: "TreeOut", budget: int, cost_fixed: float, cost_per_token: float,
+                     n_verify: torch.Tensor, rank: torch.Tensor, stream=None) -> None:
+    """How many best-first nodes of each tree to verify, and every node's
+    best-first position (see dt_verify_length in dt.h); all on the device."""
+    t = tree._c()
+    B = int(tree.n_nodes.shape[0])
+    if stream is None:
+        h = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    elif isinstance(stream, int):
+        h = stream
+    else:
+        h = stream.cuda_stream
+    st = _load().dt_verify_length(ctypes.byref(t), B, int(budget), float(cost_fixed), float(cost_per_token),
+                                  _ptr(n_verify), _ptr(rank), h)
+    if st != DT_OK:
+        raise DtError(st, "dt_verify_length")
 
 
 def dt_position_topk(logits: torch.Tensor, params: Params, lse: torch.Tensor, topk_tok: torch.Tensor,

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdt.so")
-SOURCES = ["api.hip", "sweep.hip", "tree.hip", "ngram_update.hip", "vocab.hip"]
+SOURCES = ["api.hip", "sweep.hip", "tree.hip", "ngram_update.hip", "vocab.hip", "verify.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32

@@ -466,3 +466,27 @@ extern "C" dt_status dt_ngram_update(const dt_ngram_table* table, const int32_t*
     if (launch_ngram_update(a, (hipStream_t)stream) != hipSuccess) return DT_ERR_HIP;
     return DT_OK;
 }
+
+extern "C" dt_status dt_verify_length(const dt_tree_out* tree, int32_t B, int32_t budget, double cost_fixed,
+                                      double cost_per_token, int32_t* n_verify, int32_t* rank, void* stream) {
+    if (!tree || B < 0 || budget < 1) return DT_ERR_INVALID_ARG;
+    if (!(cost_fixed > 0.0) || !isfinite(cost_fixed) || !(cost_per_token >= 0.0) || !isfinite(cost_per_token))
+        return DT_ERR_INVALID_ARG;
+    if (budget > kMaxBudget) return DT_ERR_UNSUPPORTED;
+    if (B == 0) return DT_OK;
+    if (!tree->n_nodes || !tree->parents || !tree->depths || !tree->scores || !n_verify || !rank)
+        return DT_ERR_INVALID_ARG;
+    VerifyArgs a{};
+    a.B = B;
+    a.budget = budget;
+    a.cost_fixed = cost_fixed;
+    a.cost_per_token = cost_per_token;
+    a.n_nodes = tree->n_nodes;
+    a.parents = tree->parents;
+    a.depths = tree->depths;
+    a.scores = tree->scores;
+    a.n_verify = n_verify;
+    a.rank = rank;
+    if (launch_verify(a, (hipStream_t)stream) != hipSuccess) return DT_ERR_HIP;
+    return DT_OK;
+}

@@ -238,6 +238,17 @@ struct FinishArgs {
     uint32_t* mask;
 };
 
+struct VerifyArgs {
+    int B, budget;
+    double cost_fixed, cost_per_token;
+    const int32_t* n_nodes;
+    const int32_t* parents;
+    const int32_t* depths;
+    const float* scores;
+    int32_t* n_verify;
+    int32_t* rank;
+};
+
 struct MergeArgs {
     int rows, C, k;
     const float* part_m;
@@ -264,5 +275,6 @@ hipError_t launch_vocab(const VocabArgs& a, hipStream_t stream);
 hipError_t launch_fnorm(const float* F, int V, int R, float* out, hipStream_t stream);
 hipError_t launch_frontier(const FrontierArgs& a, hipStream_t stream);
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 
 }  // namespace dt

@@ -237,6 +237,28 @@ dt_status dt_ngram_update(const dt_ngram_table* table, const int32_t* ctx, const
                           const int32_t* lengths, int32_t B, int32_t L, float new_logp,
                           int32_t* counts, void* stream);
 
+/* How many nodes of each built tree to send to verification (LibraSpec,
+ * scholarbro listing abstract: the speculative length is chosen for expected
+ * speedup and extended only while the acceptance gain outweighs the added
+ * verification cost, judged from the drafter's confidence).  Candidate
+ * verification sets are the prefixes of the tree's best-first order (a node
+ * is available once its parent is taken; the best available by score desc,
+ * depth asc, index asc is taken next; every prefix is closed under parents).
+ * Node n of that order has confidence c_n = exp(score_n); with
+ * A(n) = 1 + sum_{i<n} c_i expected tokens per round and
+ * T(n) = cost_fixed + cost_per_token * n its cost (any time unit), node n is
+ * added while c_n * T(n) > cost_per_token * A(n), i.e. while A/T strictly
+ * grows; n_verify[b] is where that stops (0..n_nodes).  rank[b][i] receives
+ * node i's best-first position, -1 for rows i >= n_nodes: verify the nodes
+ * with rank < n_verify.
+ * tree: the arrays dt_build_tree wrote ([B][budget]; tokens and mask unused).
+ * n_verify: device [B] int32; rank: device [B][budget] int32.
+ * Errors: DT_ERR_INVALID_ARG for null arrays, B < 0, budget < 1, or a cost
+ *   that is not finite, cost_fixed <= 0 or cost_per_token < 0;
+ *   DT_ERR_UNSUPPORTED for budget > 1024; DT_ERR_HIP if the launch fails. */
+dt_status dt_verify_length(const dt_tree_out* tree, int32_t B, int32_t budget, double cost_fixed,
+                           double cost_per_token, int32_t* n_verify, int32_t* rank, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -153,3 +153,23 @@ def test_ngram_update_validation():
     assert call(bd.NGram(**hk), tok=0) == bd.DT_ERR_INVALID_ARG
     assert call(bd.NGram(**hk), B=0) == bd.DT_OK                             # nothing to add: no launch
     assert call(bd.NGram(**hk), L=0, tok=0) == bd.DT_OK
+
+
+def test_verify_length_validation():
+    f = bd._load().dt_verify_length
+    t = bd._TreeOut(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+    def call(B=2, budget=8, c0=1.0, c1=1.0, nv=FAKE, rk=FAKE, tree=t):
+        return f(ctypes.byref(tree) if tree is not None else None, B, budget, c0, c1, nv, rk, 0)
+
+    assert call(tree=None) == bd.DT_ERR_INVALID_ARG
+    assert call(B=-1) == bd.DT_ERR_INVALID_ARG
+    assert call(budget=0) == bd.DT_ERR_INVALID_ARG
+    assert call(c0=0.0) == bd.DT_ERR_INVALID_ARG
+    assert call(c0=math.inf) == bd.DT_ERR_INVALID_ARG
+    assert call(c1=-0.5) == bd.DT_ERR_INVALID_ARG
+    assert call(c1=math.nan) == bd.DT_ERR_INVALID_ARG
+    assert call(nv=0) == bd.DT_ERR_INVALID_ARG
+    assert call(tree=bd._TreeOut(FAKE, FAKE, 0, FAKE, FAKE, FAKE)) == bd.DT_ERR_INVALID_ARG
+    assert call(budget=2048) == bd.DT_ERR_UNSUPPORTED
+    assert call(B=0) == bd.DT_OK                                            # nothing to do: no launch
