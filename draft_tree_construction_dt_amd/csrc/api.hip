@@ -89,6 +89,7 @@ WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s) {
     w.off_nd_s = take(nn * 8);
     w.off_part = take(fw * w.C2 * (int64_t)sizeof(VocabEntry));
     w.off_fnorm = take(full ? (int64_t)p->V * 4 : 0);
+    w.off_seed = take(full ? B * 8 : 0);
     w.total = (size_t)round_up(off, 256);
     return w;
 }
@@ -267,6 +268,7 @@ static dt_status build_full(const void* logits, const dt_params* p, const SweepP
     va.f_rk = (const double*)(ws + w.off_f_rk);
     va.f_n = (const int32_t*)(ws + w.off_f_n);
     va.part = (VocabEntry*)(ws + w.off_part);
+    va.seed = (const double*)(ws + w.off_seed);
     FrontierArgs fa{};
     fa.B = p->B;
     fa.d = p->d;
@@ -284,7 +286,18 @@ static dt_status build_full(const void* logits, const dt_params* p, const SweepP
     fa.nd_par = (int32_t*)(ws + w.off_nd_par);
     fa.nd_dep = (int32_t*)(ws + w.off_nd_dep);
     fa.nd_s = (double*)(ws + w.off_nd_s);
+    fa.V = p->V;
+    fa.k = p->k;
+    fa.R = p->R;
+    fa.ttok = ma.tok;
+    fa.tx = ma.val;
+    fa.E = p->E;
+    fa.F = p->F;
+    fa.seed = (double*)(ws + w.off_seed);
+    fa.fnorm = va.fnorm;
     if (launch_fnorm(p->F, p->V, p->R, (float*)(ws + w.off_fnorm), stream) != hipSuccess) return DT_ERR_HIP;
+    fa.t = 0;
+    if (launch_seed1(fa, p->ctx, stream) != hipSuccess) return DT_ERR_HIP;
     if (p->prof_event_start && hipEventRecord((hipEvent_t)p->prof_event_start, stream) != hipSuccess)
         return DT_ERR_HIP;
     for (int t = 1; t <= p->d; ++t) {

@@ -71,10 +71,11 @@ struct SweepPlan {
 //   nd_s                      [B][d*W]   their cumulative log-scores
 //   part                      [B][C2][W] each vocabulary chunk's top-W (VocabEntry)
 //   fnorm                     [V]        |F_v|, the screen's rounding bound
+//   seed                      [B]        a lower bound for the depth's W-th key
 struct WorkspacePlan {
     size_t off_m, off_s, off_keys, off_lse, off_ttok, off_tx, off_vmask, off_g;
     size_t off_f_tok, off_f_rk, off_f_s, off_f_node, off_f_n, off_n_tree;
-    size_t off_nd_tok, off_nd_par, off_nd_dep, off_nd_s, off_part, off_fnorm;
+    size_t off_nd_tok, off_nd_par, off_nd_dep, off_nd_s, off_part, off_fnorm, off_seed;
     size_t total;
     int n_ctx_cap;      // contexts per request the vmask area holds (the trigram count)
     int vchunk, C2;     // full-vocabulary mode: columns per chunk and chunk count
@@ -204,13 +205,20 @@ struct VocabArgs {
     const int32_t* f_tok;
     const double* f_rk;
     const int32_t* f_n;
+    const double* seed;            // [B] a lower bound for this depth's W-th key (-inf = none)
     VocabEntry* part;
 };
 
 struct FrontierArgs {
-    int B, d, W, t, C2;
+    int B, V, d, W, t, C2, k, R;
     const VocabEntry* part;
     const double* lse;
+    const int32_t* ttok;           // [B*d][k] each row's top-k tokens
+    const float* tx;               // [B*d][k] their logits
+    const float* E;
+    const float* F;
+    const float* fnorm;            // [V] |F_v|
+    double* seed;                  // [B] a lower bound for the next depth's W-th key
     int32_t* f_tok;
     double* f_rk;
     double* f_s;
@@ -274,6 +282,7 @@ hipError_t launch_ngram_update(const NGramUpdateArgs& a, hipStream_t stream);
 hipError_t launch_vocab(const VocabArgs& a, hipStream_t stream);
 hipError_t launch_fnorm(const float* F, int V, int R, float* out, hipStream_t stream);
 hipError_t launch_frontier(const FrontierArgs& a, hipStream_t stream);
+hipError_t launch_seed1(const FrontierArgs& a, const int32_t* ctx, hipStream_t stream);
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 

@@ -41,6 +41,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 extern "C" __device__ double __ockl_wfred_max_f64(double);           // DPP wavefront reductions (ROCm ockl)
 extern "C" __device__ unsigned long long __ockl_wfred_min_u64(unsigned long long);
+extern "C" __device__ int __ockl_wfred_add_i32(int);
 
 __device__ __forceinline__ unsigned long long ord64(double x) {
     const unsigned long long u = (unsigned long long)__double_as_longlong(x);
@@ -272,7 +273,8 @@ __device__ double finalize(VocabLds& L, int slot, int& cnt, int W, int lane, con
                 ve.g = G[r];
                 ve.x = X[r];
                 ve.tie = (I[r] >> 4) * 64u + (I[r] & 15u);
-                ve.pad[0] = ve.pad[1] = 0u;
+                ve.pad[0] = rank[r] == 0 ? (uint32_t)(n < W ? n : W) : 0u;   // entry 0: the list's length
+                ve.pad[1] = 0u;
                 out[rank[r]] = ve;
             }
             if (rank[r] == W - 1) lam = K[r];
@@ -357,7 +359,7 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
     float thr[kVocabReqPerWave][4];
 #pragma unroll
     for (int j = 0; j < kVocabReqPerWave; ++j) {
-        lam[j] = -INFINITY;
+        lam[j] = nf[j] > 0 ? a.seed[bq[j]] : -INFINITY;                // exact keys of real candidates
         lst[j] = -INFINITY;
         cnt[j] = 0;
         row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq]);
@@ -513,6 +515,139 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// A lower bound for a depth's W-th key before it is searched: the pairs
+// (frontier node, one of the row's top-k tokens) are real candidates of the
+// depth, so the W-th largest of their keys' lower ends bounds the W-th key of
+// all candidates from below.  g is small next to the spread of the logits,
+// so the bound is close, and the vocabulary scan then keeps little but the
+// winners.  The pairs' g come from one 16 x 16 fp32 MFMA tile per 16 tokens,
+// with the scan's interval (ak - e is below the exact key).  One wave.
+// ---------------------------------------------------------------------------
+// the token side of the pairs: the row's first 32 top-k tokens, their logits,
+// F rows and norms (independent of the frontier, so loaded early)
+template <int KS>
+struct SeedSide {
+    float f[2][KS];
+    float x[2];
+    float nf[2];
+    bool ok[2];
+};
+
+template <int KS>
+__device__ __forceinline__ void seed_side(const FrontierArgs& a, int row, int lane, SeedSide<KS>& sd) {
+    constexpr int R = 4 * KS;
+    const int m = lane & 15, kq = lane >> 4;
+    const int k = a.k;
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+        const int col = tile * 16 + m;
+        const bool cv = col < k;
+        const int64_t o = (int64_t)row * k + (cv ? col : 0);
+        const int v = cv ? a.ttok[o] : 0;
+        const float x = cv ? a.tx[o] : -INFINITY;
+        const bool vv = cv && x != -INFINITY && v >= 0 && v < a.V;
+        const int vs = vv ? v : 0;
+        const float4* fr = reinterpret_cast<const float4*>(a.F + (int64_t)vs * R + kq * KS);
+#pragma unroll
+        for (int s4 = 0; s4 < KS / 4; ++s4) {
+            const float4 q = fr[s4];
+            sd.f[tile][4 * s4 + 0] = q.x;
+            sd.f[tile][4 * s4 + 1] = q.y;
+            sd.f[tile][4 * s4 + 2] = q.z;
+            sd.f[tile][4 * s4 + 3] = q.w;
+        }
+        sd.nf[tile] = a.fnorm[vs];
+        sd.x[tile] = x;
+        sd.ok[tile] = vv;
+    }
+}
+
+// the frontier side and the bound: one 16 x 16 fp32 MFMA tile per 16
+// tokens, each pair's lower end ak - e (below its exact key), the W-th
+// largest of them
+template <int KS>
+__device__ double seed_bound(const FrontierArgs& a, const SeedSide<KS>& sd, int nfr, const int* ftok,
+                             const double* frk, int lane) {
+    constexpr int R = 4 * KS;
+    const int m = lane & 15, kq = lane >> 4;
+    const int W = a.W;
+    const int pt = m < nfr ? ftok[m] : -1;
+    float A[KS];
+    {
+        const float4* er = reinterpret_cast<const float4*>(a.E + (int64_t)(pt >= 0 ? pt : 0) * R + kq * KS);
+#pragma unroll
+        for (int s4 = 0; s4 < KS / 4; ++s4) {
+            const float4 e = pt >= 0 ? er[s4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            A[4 * s4 + 0] = e.x;
+            A[4 * s4 + 1] = e.y;
+            A[4 * s4 + 2] = e.z;
+            A[4 * s4 + 3] = e.w;
+        }
+    }
+    float ne = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) ne += A[s] * A[s];
+    ne += __shfl_xor(ne, 16);
+    ne += __shfl_xor(ne, 32);
+    float eb[4];
+    double rr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * kq + i;
+        eb[i] = 0x1p-17f * sqrtf(__shfl(ne, r)) * (1.f + 0x1p-20f);
+        rr[i] = frk[r < nfr ? r : 0];
+    }
+    double lo[2][4];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s], sd.f[tile][s], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = sd.ok[tile] && 4 * kq + i < nfr;
+            const double ak = (rr[i] + (double)sd.x[tile]) + (double)acc[i];
+            const float e = eb[i] * sd.nf[tile] + fabsf((float)ak) * 0x1p-44f + 0x1p-100f;
+            lo[tile][i] = ok ? ak - (double)e : -INFINITY;
+        }
+    }
+    // the W-th largest lower end, each rounded down to fp32 (still below the
+    // exact keys): the largest T with at least W keys >= T, bit by bit
+    uint32_t key[8];
+    int nv = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const double val = lo[q >> 2][q & 3];
+        const bool ok = val != -INFINITY;
+        key[q] = ok ? ord_bits(__float_as_uint(__double2float_rd(val))) : 0u;
+        nv += __popcll(__ballot(ok));
+    }
+    if (nv < W) return -INFINITY;                                      // fewer than W pairs
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) cnt += __popcll(__ballot(key[q] >= c));
+        if (cnt >= W) T = c;
+    }
+    return (double)__uint_as_float(unord_bits(T));
+}
+
+// depth 1: the root is the only frontier node
+template <int KS>
+__global__ void __launch_bounds__(64) seed1_kernel(FrontierArgs a, const int32_t* __restrict__ ctx) {
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int root = ctx[2 * b + 1];
+    const int tok = (unsigned)root < (unsigned)a.V ? root : -1;      // outside the vocabulary: no parent term
+    const double rk0 = 0.0;
+    SeedSide<KS> sd;
+    seed_side<KS>(a, b * a.d + 0, lane, sd);
+    const double s = seed_bound<KS>(a, sd, 1, &tok, &rk0, lane);
+    if (lane == 0) a.seed[b] = s;
+}
+
+// ---------------------------------------------------------------------------
 // frontier merge: one workgroup per request
 // ---------------------------------------------------------------------------
 constexpr int kFrontCap = 1024;
@@ -526,85 +661,163 @@ __device__ __forceinline__ bool entry_before(double ka, uint32_t ta, double kb, 
 // their heads bounds the frontier's W-th key from below (W distinct entries
 // reach it) and only entries at or above it can be selected; they are ranked
 // exactly by (Rk desc, tie asc).
+template <int KS>
 __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
     __shared__ double s_k[kFrontCap];
     __shared__ uint32_t s_t[kFrontCap];
     __shared__ int s_src[kFrontCap];
+    __shared__ double s_g[kFrontCap];
+    __shared__ float s_x[kFrontCap];
+    __shared__ int s_q[kMaxVocabChunks];
+    __shared__ int s_off[kMaxVocabChunks + 1];
     __shared__ int s_win[kFullMaxW];
+    __shared__ double s_ps[kFullMaxW];
+    __shared__ int s_pn[kFullMaxW];
+    __shared__ int s_ftok[kFullMaxW];
+    __shared__ double s_frk[kFullMaxW];
     const int b = blockIdx.x, lane = threadIdx.x;
     const int W = a.W, C2 = a.C2;
     const VocabEntry* lists = a.part + (int64_t)b * C2 * W;
+    const int64_t fb = (int64_t)b * W;
 
-    // 1. the heads, then the W-th largest of them by W extractions
+    // 0. loads that need nothing from this kernel: the previous frontier's
+    //    scores and node ids, and the token side of the next depth's bound
+    if (a.t > 1 && lane < W) {
+        s_ps[lane] = a.f_s[fb + lane];
+        s_pn[lane] = a.f_node[fb + lane];
+    }
+    SeedSide<KS> sd;
+    if (a.t < a.d) seed_side<KS>(a, b * a.d + a.t, lane, sd);
+
+    // 1. list heads with their lengths
     double hk[kHeadsPerLane];
+    int hc[kHeadsPerLane];
 #pragma unroll
     for (int q = 0; q < kHeadsPerLane; ++q) {
         const int c = lane + 64 * q;
         hk[q] = c < C2 ? lists[(int64_t)c * W].rk : -INFINITY;
+        hc[q] = c < C2 ? (int)lists[(int64_t)c * W].pad[0] : 0;
     }
-    uint32_t taken = 0;
-    double bound = -INFINITY;
-    int found = 0;
-    for (int r = 0; r < W; ++r) {
-        double lb = -INFINITY;
-        int lq = -1;
+    int mine = 0;
 #pragma unroll
-        for (int q = 0; q < kHeadsPerLane; ++q)
-            if (!((taken >> q) & 1u) && hk[q] != -INFINITY && (lq < 0 || hk[q] > lb)) {
-                lb = hk[q];
-                lq = q;
-            }
-        const double wb = wave_max_d(lq >= 0 ? lb : -INFINITY);
-        if (wb == -INFINITY) break;                                   // fewer than W heads
-        const int wl = __builtin_ctzll(__ballot(lq >= 0 && lb == wb));
-        if (lane == wl) taken |= 1u << lq;
-        bound = wb;
-        ++found;
-    }
-    if (found < W) bound = -INFINITY;
-    __syncthreads();
+    for (int q = 0; q < kHeadsPerLane; ++q) mine += hc[q];
+    const int total = __ockl_wfred_add_i32(mine);
 
-    // 2. every entry at or above the bound: the qualifying lists (head at or
-    //    above it) are read 64 entries per round, all lanes loading at once
-    __shared__ int s_q[kMaxVocabChunks];
-    int nq = 0;
-#pragma unroll
-    for (int q = 0; q < kHeadsPerLane; ++q) {
-        const int c = lane + 64 * q;
-        const bool qual = c < C2 && hk[q] != -INFINITY && hk[q] >= bound;
-        const unsigned long long m = __ballot(qual);
-        if (qual) s_q[nq + lanes_below(m)] = c;
-        nq += __popcll(m);
-    }
-    __syncthreads();
     int n = 0;
-    const int items = nq * W;
-    for (int it0 = 0; it0 < items; it0 += 64) {
-        const int it = it0 + lane;
-        double k = -INFINITY;
-        uint32_t t = 0xFFFFFFFFu;
-        int idx = 0;
-        if (it < items) {
-            const int qi = it / W, r = it - qi * W;
-            idx = s_q[qi] * W + r;
-            k = lists[idx].rk;
-            t = lists[idx].tie;
+    if (total <= kFrontCap) {
+        // 2a. every listed entry: the non-empty lists in chunk order, their
+        //     offsets, then 64 entries per round with all lanes loading
+        int nq = 0;
+#pragma unroll
+        for (int q = 0; q < kHeadsPerLane; ++q) {
+            const bool ne = hc[q] > 0;
+            const unsigned long long mq = __ballot(ne);
+            if (ne) s_q[nq + lanes_below(mq)] = (lane + 64 * q) | (hc[q] << 16);
+            nq += __popcll(mq);
         }
-        const bool take = k != -INFINITY && k >= bound;
-        const unsigned long long m = __ballot(take);
-        if (take) {
-            const int pos = n + lanes_below(m);
-            if (pos < kFrontCap) {
-                s_k[pos] = k;
-                s_t[pos] = t;
-                s_src[pos] = idx;
+        __syncthreads();
+        if (lane == 0) {
+            int o = 0;
+            for (int i = 0; i < nq; ++i) {
+                s_off[i] = o;
+                o += s_q[i] >> 16;
             }
+            s_off[nq] = o;
         }
-        n += __popcll(m);
+        __syncthreads();
+        for (int it = lane; it < total; it += 64) {
+            int lo = 0, hi = nq - 1;                                    // the list holding item it
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= it) lo = mid;
+                else hi = mid - 1;
+            }
+            const int idx = (s_q[lo] & 0xFFFF) * W + (it - s_off[lo]);
+            const VocabEntry e = lists[idx];
+            s_k[it] = e.rk;
+            s_t[it] = e.tie;
+            s_g[it] = e.g;
+            s_x[it] = e.x;
+            s_src[it] = it;
+        }
+        n = total;
+    } else {
+        // 2b. long lists: the W-th largest head bounds the frontier's W-th
+        //     key from below (W distinct entries reach it); read the entries
+        //     of the lists whose head reaches it
+        uint32_t taken = 0;
+        double bound = -INFINITY;
+        int found = 0;
+        for (int r = 0; r < W; ++r) {
+            double lb = -INFINITY;
+            int lq = -1;
+#pragma unroll
+            for (int q = 0; q < kHeadsPerLane; ++q)
+                if (!((taken >> q) & 1u) && hk[q] != -INFINITY && (lq < 0 || hk[q] > lb)) {
+                    lb = hk[q];
+                    lq = q;
+                }
+            const double wb = wave_max_d(lq >= 0 ? lb : -INFINITY);
+            if (wb == -INFINITY) break;
+            const int wl = __builtin_ctzll(__ballot(lq >= 0 && lb == wb));
+            if (lane == wl) taken |= 1u << lq;
+            bound = wb;
+            ++found;
+        }
+        if (found < W) bound = -INFINITY;
+        int nq = 0;
+#pragma unroll
+        for (int q = 0; q < kHeadsPerLane; ++q) {
+            const int c = lane + 64 * q;
+            const bool qual = c < C2 && hk[q] != -INFINITY && hk[q] >= bound;
+            const unsigned long long mq = __ballot(qual);
+            if (qual) s_q[nq + lanes_below(mq)] = c;
+            nq += __popcll(mq);
+        }
+        __syncthreads();
+        const int items = nq * W;
+        for (int it0 = 0; it0 < items; it0 += 64) {
+            const int it = it0 + lane;
+            double k = -INFINITY;
+            uint32_t t = 0xFFFFFFFFu;
+            int idx = 0;
+            if (it < items) {
+                const int qi = it / W, r = it - qi * W;
+                idx = s_q[qi] * W + r;
+                k = lists[idx].rk;
+                t = lists[idx].tie;
+            }
+            const bool take = k != -INFINITY && k >= bound;
+            const unsigned long long m = __ballot(take);
+            if (take) {
+                const int pos = n + lanes_below(m);
+                if (pos < kFrontCap) {
+                    s_k[pos] = k;
+                    s_t[pos] = t;
+                    s_g[pos] = lists[idx].g;
+                    s_x[pos] = lists[idx].x;
+                    s_src[pos] = pos;
+                }
+            }
+            n += __popcll(m);
+        }
     }
     __syncthreads();
     const int nsel = n < W ? n : W;
-    if (n <= kFrontCap) {
+    if (n <= 256) {
+        // each candidate's rank by (Rk desc, tie asc): a count over the others
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = lane + 64 * q;
+            if (i < n) {
+                const double ki = s_k[i];
+                const uint32_t ti = s_t[i];
+                int r = 0;
+                for (int j = 0; j < n; ++j) r += entry_before(s_k[j], s_t[j], ki, ti);
+                if (r < W) s_win[r] = s_src[i];
+            }
+        }
+    } else if (n <= kFrontCap) {
         // W extractions over the candidates, 16 per lane in registers
         double ck[kFrontCap / 64];
         uint32_t ct[kFrontCap / 64];
@@ -664,28 +877,41 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
                     bi = oi;
                 }
             }
-            if (lane == 0) s_win[r] = bi;
+            if (lane == 0) s_win[r] = -1 - bi;                          // a list index, not a slot
             pk = bk;
             pt = bt;
         }
     }
     __syncthreads();
 
-    // 3. the new nodes and the next frontier (parents read before any write)
+    // 3. the new nodes and the next frontier
     const int base = a.t == 1 ? 0 : a.n_tree[b];
-    const int64_t fb = (int64_t)b * W;
     int tok = 0, pnode = -1;
     double rkv = 0.0, sc = 0.0;
     if (lane < nsel) {
-        const VocabEntry& e = lists[s_win[lane]];
-        tok = (int)(e.tie >> 6);
-        const int pr = (int)(e.tie & 63u);
-        const double ps = a.t == 1 ? 0.0 : a.f_s[fb + pr];
-        pnode = a.t == 1 ? -1 : a.f_node[fb + pr];
-        rkv = e.rk;
-        sc = (ps + ((double)e.x - a.lse[(int64_t)b * a.d + (a.t - 1)])) + e.g;
+        const int w = s_win[lane];
+        double ek, eg;
+        float ex;
+        uint32_t et;
+        if (w >= 0) {                                                   // a candidate slot in LDS
+            ek = s_k[w];
+            et = s_t[w];
+            eg = s_g[w];
+            ex = s_x[w];
+        } else {
+            const VocabEntry& e = lists[-1 - w];
+            ek = e.rk;
+            et = e.tie;
+            eg = e.g;
+            ex = e.x;
+        }
+        tok = (int)(et >> 6);
+        const int pr = (int)(et & 63u);
+        const double ps = a.t == 1 ? 0.0 : s_ps[pr];
+        pnode = a.t == 1 ? -1 : s_pn[pr];
+        rkv = ek;
+        sc = (ps + ((double)ex - a.lse[(int64_t)b * a.d + (a.t - 1)])) + eg;
     }
-    __syncthreads();
     if (lane < nsel) {
         const int node = base + lane;
         const int64_t nb = (int64_t)b * a.d * W + node;
@@ -697,10 +923,18 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
         a.f_rk[fb + lane] = rkv;
         a.f_s[fb + lane] = sc;
         a.f_node[fb + lane] = node;
+        s_ftok[lane] = tok;
+        s_frk[lane] = rkv;
     }
     if (lane == 0) {
         a.f_n[b] = nsel;
         a.n_tree[b] = base + nsel;
+    }
+    // 4. a lower bound for the next depth's W-th key
+    if (a.t < a.d) {
+        __syncthreads();
+        const double bnd = nsel > 0 ? seed_bound<KS>(a, sd, nsel, s_ftok, s_frk, lane) : -INFINITY;
+        if (lane == 0) a.seed[b] = bnd;
     }
 }
 
@@ -754,9 +988,23 @@ hipError_t launch_vocab(const VocabArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+hipError_t launch_seed1(const FrontierArgs& a, const int32_t* ctx, hipStream_t stream) {
+    if (a.B <= 0) return hipSuccess;
+    const dim3 grid((unsigned)a.B), block(64);
+    if (a.R == 16) hipLaunchKernelGGL(seed1_kernel<4>, grid, block, 0, stream, a, ctx);
+    else if (a.R == 32) hipLaunchKernelGGL(seed1_kernel<8>, grid, block, 0, stream, a, ctx);
+    else if (a.R == 64) hipLaunchKernelGGL(seed1_kernel<16>, grid, block, 0, stream, a, ctx);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_frontier(const FrontierArgs& a, hipStream_t stream) {
     if (a.B <= 0) return hipSuccess;
-    hipLaunchKernelGGL(frontier_kernel, dim3((unsigned)a.B), dim3(64), 0, stream, a);
+    const dim3 grid((unsigned)a.B), block(64);
+    if (a.R == 16) hipLaunchKernelGGL(frontier_kernel<4>, grid, block, 0, stream, a);
+    else if (a.R == 32) hipLaunchKernelGGL(frontier_kernel<8>, grid, block, 0, stream, a);
+    else if (a.R == 64) hipLaunchKernelGGL(frontier_kernel<16>, grid, block, 0, stream, a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
