@@ -19,14 +19,13 @@
 // batch (a ballot radix selection, no data exchange between lanes) and raised
 // by selections of the buffer.
 #include "common.h"
+#include "wave.h"
 
 namespace dt {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-extern "C" __device__ float __ockl_wfred_max_f32(float);      // DPP wavefront reductions (ROCm ockl)
-extern "C" __device__ double __ockl_wfred_add_f64(double);
 constexpr int U = kSweepVecsPerThread;
 typedef uint32_t vec4 __attribute__((ext_vector_type(4)));
 constexpr int CAP = kSweepCap;
@@ -309,9 +308,9 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
 
     // ---- this wave's partial: its top-k sorted, and (max, sum exp(x - max))
     wave_select(buf, st, k, lane);
-    const float M = __ockl_wfred_max_f32(st.m);
+    const float M = wave_max_f32(st.m);
     const double sl = (st.m == -INFINITY) ? 0.0 : st.s * (double)__builtin_amdgcn_exp2f((st.m - M) * kLog2e);
-    const double S = __ockl_wfred_add_f64(sl);
+    const double S = wave_add_f64(sl);
     if (a.lists == kWaves) {
         // every wave writes its own list, so waves never wait for each other
         const int64_t list = (row * a.C + chunk) * kWaves + wave;
@@ -338,10 +337,10 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
     const int n = kWaves * k, n8 = (n + 7) & ~7;
     if (lane < n8 - n) s_all[n + lane] = 0ull;          // pad: 0 beats nothing
     const float mw = lane < kWaves ? s_wm[lane] : -INFINITY;
-    const float Mall = __ockl_wfred_max_f32(mw);
+    const float Mall = wave_max_f32(mw);
     const double sw = (lane < kWaves && mw != -INFINITY)
                           ? s_ws[lane] * (double)__builtin_amdgcn_exp2f((mw - Mall) * kLog2e) : 0.0;
-    const double Sall = __ockl_wfred_add_f64(sw);
+    const double Sall = wave_add_f64(sw);
     const unsigned long long ka = lane < n ? s_all[lane] : 0ull;
     const unsigned long long kb = lane + 64 < n ? s_all[lane + 64] : 0ull;
     int ra = 0, rb = 0;

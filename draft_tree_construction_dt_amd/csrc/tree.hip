@@ -33,11 +33,11 @@
 //  6. Compact in BFS order, remap parents and pack the ancestor mask used by
 //     tree-attention verification.
 #include "common.h"
+#include "wave.h"
 
 namespace dt {
 namespace {
 typedef double v4d __attribute__((ext_vector_type(4)));
-extern "C" __device__ double __ockl_wfred_min_f64(double);
 constexpr unsigned long long kEmptyKey = 0xFFFFFFFFFFFFFFFFull;
 
 __device__ __forceinline__ float key_value(unsigned long long key) {
@@ -50,11 +50,6 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-extern "C" __device__ float __ockl_wfred_max_f32(float);      // DPP wavefront reductions (ROCm ockl)
-extern "C" __device__ double __ockl_wfred_add_f64(double);
-extern "C" __device__ unsigned long long __ockl_wfred_max_u64(unsigned long long);
-extern "C" __device__ unsigned long long __ockl_wfred_min_u64(unsigned long long);
-extern "C" __device__ int __ockl_wfred_add_i32(int);
 
 __device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
     // SplitMix64 output function (Steele, Lea, Flood).
@@ -91,14 +86,14 @@ __device__ void merge_row(const float* __restrict__ part_m, const double* __rest
     }
 
     // normaliser: max and rescaled sum over the lists, log in fp64
-    const float M = __ockl_wfred_max_f32(fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3])));
+    const float M = wave_max_f32(fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3])));
     double sum = 0.0;
     if (M != -INFINITY) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if (mc[q] != -INFINITY) sum += sc[q] * (double)__builtin_amdgcn_exp2f((mc[q] - M) * 1.4426950408889634f);
     }
-    sum = __ockl_wfred_add_f64(sum);
+    sum = wave_add_f64(sum);
     if (lane == 0) {
         // the true normaliser is >= the row max; clamp the rounding of a sum
         // whose largest term is 1 so that every log-probability stays <= 0
@@ -124,9 +119,9 @@ __device__ void merge_row(const float* __restrict__ part_m, const double* __rest
             }
         }
     }
-    bk = __ockl_wfred_max_u64(bk);
-    bq = __ockl_wfred_min_u64(bq);
-    nq = __ockl_wfred_add_i32(nq);
+    bk = wave_max_u64(bk);
+    bq = wave_min_u64(bq);
+    nq = wave_add_i32(nq);
     unsigned long long th = bk;
     if (nq * q >= k && bq > th) th = bq;
     int ns = 0;
@@ -873,7 +868,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
                     kcm[r] = s_vmask[ci];
                 }
             }
-            const double lb = nfirst >= W ? __ockl_wfred_min_f64(firstmin) : -INFINITY;
+            const double lb = nfirst >= W ? wave_min_f64(firstmin) : -INFINITY;
             int ns = 0;
 #pragma unroll
             for (int r = 0; r < RM; ++r) {

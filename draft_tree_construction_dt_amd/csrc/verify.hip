@@ -17,12 +17,11 @@
 #include <math.h>
 
 #include "common.h"
+#include "wave.h"
 
 namespace dt {
 namespace {
 
-extern "C" __device__ float __ockl_wfred_max_f32(float);   // DPP wavefront reductions (ROCm ockl)
-extern "C" __device__ int __ockl_wfred_min_i32(int);
 
 constexpr int kPerLane = kMaxBudget / 64;
 constexpr int kNone = 0x7FFFFFFF;
@@ -95,11 +94,11 @@ __global__ void __launch_bounds__(64) verify_kernel(VerifyArgs a) {
                 }
             }
         }
-        const float ms = __ockl_wfred_max_f32(bi != kNone ? bs : -INFINITY);
+        const float ms = wave_max_f32(bi != kNone ? bs : -INFINITY);
         const bool m1 = bi != kNone && bs == ms;
-        const int md = __ockl_wfred_min_i32(m1 ? bd : kNone);
+        const int md = wave_min_i32(m1 ? bd : kNone);
         const bool m2 = m1 && bd == md;
-        const int mi = __ockl_wfred_min_i32(m2 ? bi : kNone);
+        const int mi = wave_min_i32(m2 ? bi : kNone);
         if (mi == kNone) {                                              // only a malformed tree (a parent
             n = step;                                                   // not among its nodes) gets here
             break;

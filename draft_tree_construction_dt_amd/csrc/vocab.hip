@@ -33,15 +33,13 @@
 //                    next frontier.
 // The budget and the outputs are then the tree kernel's (finish_kernel).
 #include "common.h"
+#include "wave.h"
 
 namespace dt {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-extern "C" __device__ double __ockl_wfred_max_f64(double);           // DPP wavefront reductions (ROCm ockl)
-extern "C" __device__ unsigned long long __ockl_wfred_min_u64(unsigned long long);
-extern "C" __device__ int __ockl_wfred_add_i32(int);
 
 __device__ __forceinline__ unsigned long long ord64(double x) {
     const unsigned long long u = (unsigned long long)__double_as_longlong(x);
@@ -78,7 +76,7 @@ __device__ __forceinline__ double shfl_d(double v, int src) {
     return __longlong_as_double(((long long)hi << 32) | (uint32_t)lo);
 }
 
-__device__ __forceinline__ double wave_max_d(double v) { return __ockl_wfred_max_f64(v); }
+__device__ __forceinline__ double wave_max_d(double v) { return wave_max_f64(v); }
 
 __device__ __forceinline__ int lanes_below(unsigned long long m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -701,7 +699,7 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
     int mine = 0;
 #pragma unroll
     for (int q = 0; q < kHeadsPerLane; ++q) mine += hc[q];
-    const int total = __ockl_wfred_add_i32(mine);
+    const int total = wave_add_i32(mine);
 
     int n = 0;
     if (total <= kFrontCap) {
@@ -841,7 +839,7 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
                 }
             const double mk = wave_max_d(bq >= 0 ? bk : -INFINITY);
             const bool atk = bq >= 0 && bk == mk;
-            const unsigned long long mt = __ockl_wfred_min_u64(atk ? (unsigned long long)bt : ~0ull);
+            const unsigned long long mt = wave_min_u64(atk ? (unsigned long long)bt : ~0ull);
             const int bl = __builtin_ctzll(__ballot(atk && (unsigned long long)bt == mt));
             if (lane == bl) {
                 used |= 1u << bq;

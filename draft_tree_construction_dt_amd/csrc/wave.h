@@ -1,0 +1,120 @@
+// Wave64 reductions for gfx950: a DPP butterfly inside each 16-lane row
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror:
+// every step pairs lanes holding disjoint partial results), then the four
+// row results read into scalar registers and combined.  Every lane gets the
+// same (wave-uniform) result.  Max, min and integer sums are exact; a
+// floating-point sum is taken in this fixed order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dt {
+
+__device__ __forceinline__ int dpp_step(int v, int ctrl) {
+    switch (ctrl) {
+    case 0: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    case 1: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    default: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); // row_mirror
+    }
+}
+
+__device__ __forceinline__ uint64_t dpp_step64(uint64_t v, int ctrl) {
+    const uint32_t lo = (uint32_t)dpp_step((int)(uint32_t)v, ctrl);
+    const uint32_t hi = (uint32_t)dpp_step((int)(uint32_t)(v >> 32), ctrl);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v = fmaxf(v, __int_as_float(dpp_step(__float_as_int(v), s)));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        v = fmax(v, __longlong_as_double((long long)dpp_step64((uint64_t)__double_as_longlong(v), s)));
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const double a = __longlong_as_double((long long)readlane64(u, 0));
+    const double b = __longlong_as_double((long long)readlane64(u, 16));
+    const double c = __longlong_as_double((long long)readlane64(u, 32));
+    const double d = __longlong_as_double((long long)readlane64(u, 48));
+    return fmax(fmax(a, b), fmax(c, d));
+}
+
+__device__ __forceinline__ double wave_min_f64(double v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        v = fmin(v, __longlong_as_double((long long)dpp_step64((uint64_t)__double_as_longlong(v), s)));
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const double a = __longlong_as_double((long long)readlane64(u, 0));
+    const double b = __longlong_as_double((long long)readlane64(u, 16));
+    const double c = __longlong_as_double((long long)readlane64(u, 32));
+    const double d = __longlong_as_double((long long)readlane64(u, 48));
+    return fmin(fmin(a, b), fmin(c, d));
+}
+
+__device__ __forceinline__ double wave_add_f64(double v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v += __longlong_as_double((long long)dpp_step64((uint64_t)__double_as_longlong(v), s));
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const double a = __longlong_as_double((long long)readlane64(u, 0));
+    const double b = __longlong_as_double((long long)readlane64(u, 16));
+    const double c = __longlong_as_double((long long)readlane64(u, 32));
+    const double d = __longlong_as_double((long long)readlane64(u, 48));
+    return (a + b) + (c + d);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint64_t o = dpp_step64(v, s);
+        v = o > v ? o : v;
+    }
+    uint64_t r = readlane64(v, 0);
+    const uint64_t b = readlane64(v, 16), c = readlane64(v, 32), d = readlane64(v, 48);
+    r = b > r ? b : r;
+    r = c > r ? c : r;
+    return d > r ? d : r;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint64_t o = dpp_step64(v, s);
+        v = o < v ? o : v;
+    }
+    uint64_t r = readlane64(v, 0);
+    const uint64_t b = readlane64(v, 16), c = readlane64(v, 32), d = readlane64(v, 48);
+    r = b < r ? b : r;
+    r = c < r ? c : r;
+    return d < r ? d : r;
+}
+
+__device__ __forceinline__ int wave_add_i32(int v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v += dpp_step(v, s);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v = min(v, dpp_step(v, s));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+}  // namespace dt
