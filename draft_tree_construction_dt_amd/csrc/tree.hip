@@ -868,7 +868,29 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
                     kcm[r] = s_vmask[ci];
                 }
             }
-            const double lb = nfirst >= W ? wave_min_f64(firstmin) : -INFINITY;
+            double lb = nfirst >= W ? wave_min_f64(firstmin) : -INFINITY;
+            // With many candidates above that bound (no continuity filter, or
+            // a parent term that reorders a parent's children), tighten it:
+            // the W-th largest of the lanes' best keys, each rounded down to
+            // fp32, is reached by W distinct candidates, so it bounds the
+            // depth's W-th key from below too.  Found bit by bit with ballots
+            // over the order-preserving bits of the rounded values.
+            int nin = 0;
+#pragma unroll
+            for (int r = 0; r < RM; ++r) nin += __popcll(__ballot(kok[r] && krk[r] >= lb));
+            if (nin > 32) {
+                double lm = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < RM; ++r)
+                    if (kok[r]) lm = fmax(lm, krk[r]);
+                const uint32_t u = ord_bits(__float_as_uint(__double2float_rd(lm) + 0.0f));
+                uint32_t th = 0;
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t c = th | (1u << bit);
+                    if (__popcll(__ballot(u >= c)) >= W) th = c;
+                }
+                lb = fmax(lb, (double)__uint_as_float(unord_bits(th)));
+            }
             int ns = 0;
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
