@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 BATCH = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_traffic.json")
 SWEEP_SOURCES = [os.path.join(ROOT, "draft_tree_construction_dt_amd", "csrc", f)
-                 for f in ("sweep.hip", "common.h")]
+                 for f in ("sweep.hip", "common.h", "wave.h")]
 
 
 def parse():
@@ -66,6 +66,9 @@ def parse():
                          "(c1, c2, c2p, c3, c3p, c4, c4L, c4Lp, c5, c5f)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--traffic-from", default="",
+                    help="only write the sweep's HBM traffic file from rocprofv3 counter runs under this "
+                         "directory (subdirectories fetch, write, cfetch, cwrite; no GPU needed)")
     return ap.parse_args()
 
 
@@ -137,6 +140,60 @@ class TimingEvents:
         rc = self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream))
         if rc != 0:
             raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+
+def _counter_rows(d: str, counter: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {d}")
+    return rows
+
+
+def write_traffic(root: str, commands: list) -> None:
+    """HBM bytes per B=64 sweep launch from two counter runs of the bench
+    (FETCH_SIZE, WRITE_SIZE: KiB per dispatch) and the same counters over a
+    plain device copy of known size, whose readings give each counter's
+    scale to bytes."""
+    import statistics
+    grid = BATCH * 8 * 256                       # B=64 rows x 1 chunk x 256 threads
+    def sweep_avg(sub, counter):
+        v = [x for n, g, x in _counter_rows(os.path.join(root, sub), counter) if "sweep_kernel" in n and g == grid]
+        if not v:
+            raise SystemExit(f"no B=64 sweep dispatches in {sub}")
+        return statistics.mean(v)
+    def copy_max(sub, counter):
+        v = [(g, x) for n, g, x in _counter_rows(os.path.join(root, sub), counter) if "copyBuffer" in n]
+        g = max(g for g, _ in v)
+        return statistics.mean(x for gg, x in v if gg == g)
+    copy_bytes = None
+    with open(os.path.join(root, "copy.json")) as fh:
+        for line in fh:
+            if line.startswith("{") and "copy_probe_bytes_read" in line:
+                copy_bytes = json.loads(line)["copy_probe_bytes_read"]
+    if copy_bytes is None:
+        raise SystemExit("copy.json holds no copy probe line")
+    fetch_kib, write_kib = sweep_avg("fetch", "FETCH_SIZE"), sweep_avg("write", "WRITE_SIZE")
+    fscale = copy_bytes / (copy_max("cfetch", "FETCH_SIZE") * 1024)
+    wscale = copy_bytes / (copy_max("cwrite", "WRITE_SIZE") * 1024)
+    t = {
+        "kernel": "sweep_kernel<bf16>", "workload": "B=64, V=151936, d=8, bf16",
+        "kernel_sources_sha256": kernel_sources_hash(),
+        "fetch_size_kib": fetch_kib, "write_size_kib": write_kib,
+        "fetch_scale": fscale, "write_scale": wscale,
+        "bytes_per_launch": fetch_kib * 1024 * fscale + write_kib * 1024 * wscale,
+        "fetched_bytes": fetch_kib * 1024 * fscale, "written_bytes": write_kib * 1024 * wscale,
+        "commands": commands,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+    print(json.dumps(t))
 
 
 def copy_probe(mib: int) -> None:
@@ -335,6 +392,18 @@ def main():
         print("bench.py measures the single-GPU path only; --gpus must be 1 "
               "(requests shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:
+        r = "$R/" + os.path.relpath(args.traffic_from, ROOT)
+        write_traffic(args.traffic_from, [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {r}/fetch -o bench -- python3 $R/bench.py "
+            "--steps 20 --warmup 5 --b1-steps 10 --update-steps 20 --no-cpu --streams 1",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {r}/write -o bench -- python3 $R/bench.py "
+            "--steps 20 --warmup 5 --b1-steps 10 --update-steps 20 --no-cpu --streams 1",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {r}/cfetch -o copy -- python3 $R/bench.py "
+            f"--copy-probe-mib 1024 > {r}/copy.json",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {r}/cwrite -o copy -- python3 $R/bench.py "
+            "--copy-probe-mib 1024"])
+        return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
         return

@@ -174,13 +174,22 @@ __device__ __forceinline__ void consume(const float (&xs)[NE], int id0, int id_s
         // the four seeds can be among the row's top k, and every wave filters
         // with that one.  (All waves of the workgroup take their first batch
         // in the same call, so the barrier is reached by all of them.)
+        // A second seed: if every wave has q = ceil(k/4) lanes at or above
+        // some value, the four waves together hold k elements there.
         const float t = wave_threshold(bm, k);
-        if (lane == 0) seeds[wave] = t;
+        const float tq = wave_threshold(bm, (k + kWaves - 1) / kWaves);
+        if (lane == 0) {
+            seeds[wave] = t;
+            seeds[kWaves + wave] = tq;
+        }
         __syncthreads();
-        float tm = seeds[0];
+        float tm = seeds[0], qm = seeds[kWaves];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) tm = fmaxf(tm, seeds[w]);
-        st.thv = tm;
+        for (int w = 1; w < kWaves; ++w) {
+            tm = fmaxf(tm, seeds[w]);
+            qm = fminf(qm, seeds[kWaves + w]);
+        }
+        st.thv = fmaxf(tm, qm);
         st.thid = 0xFFFFFFFFu;
         st.fresh = false;
     }
@@ -222,7 +231,7 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
 
     __shared__ unsigned long long s_buf[kWaves][CAP];
     __shared__ float s_stage[kWaves][NE * 64];   // rare-path staging of a batch
-    __shared__ float s_seeds[kWaves];             // first-batch thresholds of the waves
+    __shared__ float s_seeds[2 * kWaves];         // first-batch thresholds of the waves (k-th, ceil(k/4)-th)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -40,17 +40,6 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-
-__device__ __forceinline__ unsigned long long ord64(double x) {
-    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
-    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-
-__device__ __forceinline__ double unord64(unsigned long long o) {
-    const unsigned long long u = (o >> 63) ? (o & 0x7FFFFFFFFFFFFFFFull) : ~o;
-    return __longlong_as_double((long long)u);
-}
-
 // raw logit bits (bf16 zero-extended, or fp32), widened only where used, so
 // that a prefetch is not waited for at the load
 template <int DT>
@@ -70,30 +59,10 @@ __device__ __forceinline__ float load_logit(const void* base, int64_t i) {
     return ((const float*)base)[i];
 }
 
-__device__ __forceinline__ double shfl_d(double v, int src) {
-    const long long u = __double_as_longlong(v);
-    const int lo = __shfl((int)(u & 0xFFFFFFFFll), src), hi = __shfl((int)(u >> 32), src);
-    return __longlong_as_double(((long long)hi << 32) | (uint32_t)lo);
-}
-
 __device__ __forceinline__ double wave_max_d(double v) { return wave_max_f64(v); }
 
 __device__ __forceinline__ int lanes_below(unsigned long long m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// the kth largest of the wave's 4 x 64 keys (key 0 = no candidate): the
-// largest T with at least kth keys >= T, found bit by bit from the top
-__device__ unsigned long long wave_kth_key(const unsigned long long (&key)[4], int kth) {
-    unsigned long long T = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-        const unsigned long long c = T | (1ull << bit);
-        int n = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) n += __popcll(__ballot(key[i] >= c));
-        if (n >= kth) T = c;
-    }
-    return T;
 }
 
 // the kth largest of the wave's 4 x 64 32-bit keys (key 0 = no candidate)
