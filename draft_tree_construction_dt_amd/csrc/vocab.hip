@@ -529,28 +529,29 @@ __device__ __forceinline__ void seed_side(const FrontierArgs& a, int row, int la
     }
 }
 
-// the frontier side and the bound: one 16 x 16 fp32 MFMA tile per 16
-// tokens, each pair's lower end ak - e (below its exact key), the W-th
-// largest of them
+// the frontier side: lane (m, kq) holds quarter kq of E[tok] for frontier
+// node m (zeros when tok < 0)
 template <int KS>
-__device__ double seed_bound(const FrontierArgs& a, const SeedSide<KS>& sd, int nfr, const int* ftok,
-                             const double* frk, int lane) {
+__device__ __forceinline__ void load_erow(const FrontierArgs& a, int tok, int kq, float (&A)[KS]) {
     constexpr int R = 4 * KS;
-    const int m = lane & 15, kq = lane >> 4;
-    const int W = a.W;
-    const int pt = m < nfr ? ftok[m] : -1;
-    float A[KS];
-    {
-        const float4* er = reinterpret_cast<const float4*>(a.E + (int64_t)(pt >= 0 ? pt : 0) * R + kq * KS);
+    const float4* er = reinterpret_cast<const float4*>(a.E + (int64_t)(tok >= 0 ? tok : 0) * R + kq * KS);
 #pragma unroll
-        for (int s4 = 0; s4 < KS / 4; ++s4) {
-            const float4 e = pt >= 0 ? er[s4] : make_float4(0.f, 0.f, 0.f, 0.f);
-            A[4 * s4 + 0] = e.x;
-            A[4 * s4 + 1] = e.y;
-            A[4 * s4 + 2] = e.z;
-            A[4 * s4 + 3] = e.w;
-        }
+    for (int s4 = 0; s4 < KS / 4; ++s4) {
+        const float4 e = tok >= 0 ? er[s4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        A[4 * s4 + 0] = e.x;
+        A[4 * s4 + 1] = e.y;
+        A[4 * s4 + 2] = e.z;
+        A[4 * s4 + 3] = e.w;
     }
+}
+
+// the bound: one 16 x 16 fp32 MFMA tile per 16 tokens, each pair's lower end
+// ak - e (below its exact key), the W-th largest of them
+template <int KS>
+__device__ double seed_bound(const FrontierArgs& a, const SeedSide<KS>& sd, int nfr, const float (&A)[KS],
+                             const double* frk, int lane) {
+    const int kq = lane >> 4;
+    const int W = a.W;
     float ne = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) ne += A[s] * A[s];
@@ -578,25 +579,24 @@ __device__ double seed_bound(const FrontierArgs& a, const SeedSide<KS>& sd, int 
             lo[tile][i] = ok ? ak - (double)e : -INFINITY;
         }
     }
-    // the W-th largest lower end, each rounded down to fp32 (still below the
-    // exact keys): the largest T with at least W keys >= T, bit by bit
-    uint32_t key[8];
-    int nv = 0;
+    // the W-th largest of the lanes' two best lower ends, each rounded down
+    // to fp32 (still below the exact keys; W distinct pairs reach it): the
+    // largest T with at least W of those values >= T, bit by bit
+    double b1 = -INFINITY, b2 = -INFINITY;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        const double val = lo[q >> 2][q & 3];
-        const bool ok = val != -INFINITY;
-        key[q] = ok ? ord_bits(__float_as_uint(__double2float_rd(val))) : 0u;
-        nv += __popcll(__ballot(ok));
+        const double v = lo[q >> 2][q & 3];
+        b2 = fmax(b2, fmin(b1, v));
+        b1 = fmax(b1, v);
     }
-    if (nv < W) return -INFINITY;                                      // fewer than W pairs
+    const bool ok1 = b1 != -INFINITY, ok2 = b2 != -INFINITY;
+    if (__popcll(__ballot(ok1)) + __popcll(__ballot(ok2)) < W) return -INFINITY;   // fewer than W pairs
+    const uint32_t k1 = ok1 ? ord_bits(__float_as_uint(__double2float_rd(b1))) : 0u;
+    const uint32_t k2 = ok2 ? ord_bits(__float_as_uint(__double2float_rd(b2))) : 0u;
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t c = T | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) cnt += __popcll(__ballot(key[q] >= c));
-        if (cnt >= W) T = c;
+        if (__popcll(__ballot(k1 >= c)) + __popcll(__ballot(k2 >= c)) >= W) T = c;
     }
     return (double)__uint_as_float(unord_bits(T));
 }
@@ -610,7 +610,9 @@ __global__ void __launch_bounds__(64) seed1_kernel(FrontierArgs a, const int32_t
     const double rk0 = 0.0;
     SeedSide<KS> sd;
     seed_side<KS>(a, b * a.d + 0, lane, sd);
-    const double s = seed_bound<KS>(a, sd, 1, &tok, &rk0, lane);
+    float A[KS];
+    load_erow<KS>(a, (lane & 15) < 1 ? tok : -1, lane >> 4, A);
+    const double s = seed_bound<KS>(a, sd, 1, A, &rk0, lane);
     if (lane == 0) a.seed[b] = s;
 }
 
@@ -655,6 +657,7 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
     }
     SeedSide<KS> sd;
     if (a.t < a.d) seed_side<KS>(a, b * a.d + a.t, lane, sd);
+    const double lse_t = a.lse[(int64_t)b * a.d + (a.t - 1)];
 
     // 1. list heads with their lengths
     double hk[kHeadsPerLane];
@@ -772,16 +775,29 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
     __syncthreads();
     const int nsel = n < W ? n : W;
     if (n <= 256) {
-        // each candidate's rank by (Rk desc, tie asc): a count over the others
+        // each candidate's rank by (Rk desc, tie asc): a count over the
+        // others, sixteen broadcast reads at a time
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int i = lane + 64 * q;
-            if (i < n) {
-                const double ki = s_k[i];
-                const uint32_t ti = s_t[i];
+            if (64 * q < n) {
+                const int ic = i < n ? i : 0;
+                const double ki = s_k[ic];
+                const uint32_t ti = s_t[ic];
                 int r = 0;
-                for (int j = 0; j < n; ++j) r += entry_before(s_k[j], s_t[j], ki, ti);
-                if (r < W) s_win[r] = s_src[i];
+                for (int j0 = 0; j0 < n; j0 += 16) {
+                    double kj[16];
+                    uint32_t tj[16];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        const int j = j0 + u < n ? j0 + u : ic;          // itself: never before itself
+                        kj[u] = s_k[j];
+                        tj[u] = s_t[j];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) r += entry_before(kj[u], tj[u], ki, ti);
+                }
+                if (i < n && r < W) s_win[r] = s_src[i];
             }
         }
     } else if (n <= kFrontCap) {
@@ -877,7 +893,7 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
         const double ps = a.t == 1 ? 0.0 : s_ps[pr];
         pnode = a.t == 1 ? -1 : s_pn[pr];
         rkv = ek;
-        sc = (ps + ((double)ex - a.lse[(int64_t)b * a.d + (a.t - 1)])) + eg;
+        sc = (ps + ((double)ex - lse_t)) + eg;
     }
     if (lane < nsel) {
         const int node = base + lane;
@@ -900,7 +916,10 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
     // 4. a lower bound for the next depth's W-th key
     if (a.t < a.d) {
         __syncthreads();
-        const double bnd = nsel > 0 ? seed_bound<KS>(a, sd, nsel, s_ftok, s_frk, lane) : -INFINITY;
+        const int m = lane & 15, kq = lane >> 4;
+        float A[KS];
+        load_erow<KS>(a, m < nsel ? s_ftok[m] : -1, kq, A);
+        const double bnd = nsel > 0 ? seed_bound<KS>(a, sd, nsel, A, s_frk, lane) : -INFINITY;
         if (lane == 0) a.seed[b] = bnd;
     }
 }
