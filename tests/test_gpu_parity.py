@@ -224,6 +224,22 @@ def test_hash_wide_rows_large_k_and_many_survivors(device, oracle_lib):
         _parity(p, device, oracle_lib, label=f"no table W={W} k={k}")
 
 
+def test_tight_bound_many_candidates(device, oracle_lib):
+    """Depths where more than 32 candidates reach the first-valid-child
+    bound (no table, and in DARTree mode a strong parent term that reorders
+    each parent's children): the depth loop then bounds the W-th key by the
+    W-th largest of the lanes' best keys rounded down to fp32.  Continuous
+    and bf16 logits, up to eight candidate slots per lane."""
+    rng = np.random.default_rng(41)
+    cases = [(MODE_DART, 16, 16), (MODE_DARTREE, 16, 16), (MODE_DARTREE, 8, 32), (MODE_DART, 24, 20)]
+    for trial, (mode, W, k) in enumerate(cases):
+        p = synth.random_problem(rng, B=3, V=700, d=5, k=k, W=W, budget=5 * W, mode=mode, R=8,
+                                 dtype=synth.DTYPE_BF16 if trial % 2 else synth.DTYPE_F32)
+        if mode == MODE_DARTREE:
+            p.E *= 4
+        _parity(p, device, oracle_lib, label=f"many candidates mode={mode} W={W} k={k}")
+
+
 def test_zero_requests(device):
     import torch
     from draft_tree_construction_dt_amd import binding as bd
