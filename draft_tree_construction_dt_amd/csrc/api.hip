@@ -89,6 +89,7 @@ WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s) {
     w.off_nd_s = take(nn * 8);
     w.off_part = take(fw * w.C2 * (int64_t)sizeof(VocabEntry));
     w.off_fnorm = take(full ? (int64_t)p->V * 4 : 0);
+    w.off_fbf = take(full ? (int64_t)p->V * p->R * 2 : 0);
     w.off_seed = take(full ? B * 8 : 0);
     w.total = (size_t)round_up(off, 256);
     return w;
@@ -263,6 +264,7 @@ static dt_status build_full(const void* logits, const dt_params* p, const SweepP
     va.E = p->E;
     va.F = p->F;
     va.fnorm = (const float*)(ws + w.off_fnorm);
+    va.Fbf = (const uint16_t*)(ws + w.off_fbf);
     va.ctx = p->ctx;
     va.f_tok = (const int32_t*)(ws + w.off_f_tok);
     va.f_rk = (const double*)(ws + w.off_f_rk);
@@ -295,7 +297,8 @@ static dt_status build_full(const void* logits, const dt_params* p, const SweepP
     fa.F = p->F;
     fa.seed = (double*)(ws + w.off_seed);
     fa.fnorm = va.fnorm;
-    if (launch_fnorm(p->F, p->V, p->R, (float*)(ws + w.off_fnorm), stream) != hipSuccess) return DT_ERR_HIP;
+    if (launch_fnorm(p->F, p->V, p->R, (float*)(ws + w.off_fnorm), (uint16_t*)(ws + w.off_fbf), stream) != hipSuccess)
+        return DT_ERR_HIP;
     fa.t = 0;
     if (launch_seed1(fa, p->ctx, stream) != hipSuccess) return DT_ERR_HIP;
     if (p->prof_event_start && hipEventRecord((hipEvent_t)p->prof_event_start, stream) != hipSuccess)

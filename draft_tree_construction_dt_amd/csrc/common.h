@@ -75,7 +75,7 @@ struct SweepPlan {
 struct WorkspacePlan {
     size_t off_m, off_s, off_keys, off_lse, off_ttok, off_tx, off_vmask, off_g;
     size_t off_f_tok, off_f_rk, off_f_s, off_f_node, off_f_n, off_n_tree;
-    size_t off_nd_tok, off_nd_par, off_nd_dep, off_nd_s, off_part, off_fnorm, off_seed;
+    size_t off_nd_tok, off_nd_par, off_nd_dep, off_nd_s, off_part, off_fnorm, off_fbf, off_seed;
     size_t total;
     int n_ctx_cap;      // contexts per request the vmask area holds (the trigram count)
     int vchunk, C2;     // full-vocabulary mode: columns per chunk and chunk count
@@ -201,6 +201,7 @@ struct VocabArgs {
     const float* E;
     const float* F;
     const float* fnorm;            // |F_v| (slightly rounded up), [V]
+    const uint16_t* Fbf;           // F rounded to bf16 (nearest even), [V][R]
     const int32_t* ctx;
     const int32_t* f_tok;
     const double* f_rk;
@@ -280,7 +281,7 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_ngram_update(const NGramUpdateArgs& a, hipStream_t stream);
 hipError_t launch_vocab(const VocabArgs& a, hipStream_t stream);
-hipError_t launch_fnorm(const float* F, int V, int R, float* out, hipStream_t stream);
+hipError_t launch_fnorm(const float* F, int V, int R, float* out, uint16_t* fbf, hipStream_t stream);
 hipError_t launch_frontier(const FrontierArgs& a, hipStream_t stream);
 hipError_t launch_seed1(const FrontierArgs& a, const int32_t* ctx, hipStream_t stream);
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);

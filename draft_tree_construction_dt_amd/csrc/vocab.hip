@@ -14,17 +14,21 @@
 //  vocab_kernel    - one workgroup per (vocabulary chunk, group of 8 requests),
 //                    a wave per 2 requests.  The dense part, G = E_frontier .
 //                    F_chunk^T for 16 frontier rows x 16 tokens per step, runs
-//                    on fp32 MFMA (v_mfma_f32_16x16x4f32).  fp32 decides
-//                    nothing: every candidate carries an interval around its
-//                    fp64 key, ak +- e with e = 2^-17 |E_p| |F_v| + |ak| 2^-44
-//                    (a product meets at most 1 + 3 + R/4 <= 20 roundings of
-//                    2^-24 on its way into an MFMA output, and
+//                    on bf16 MFMA (v_mfma_f32_16x16x32_bf16; F is rounded to
+//                    bf16 once per call, E rows when they are loaded).  The
+//                    matrix cores decide nothing: every candidate carries an
+//                    interval around its fp64 key, ak +- e with
+//                    e = 1.125 * 2^-7 |E_p| |F_v| + |ak| 2^-44 (rounding both
+//                    operands to bf16 moves each product by at most
+//                    (2^-7 + 2^-16) |E_k F_k|, the fp32 accumulation adds at
+//                    most about 2^-18 of the sum, and
 //                    sum |E_k F_k| <= |E_p| |F_v|), so a candidate is
 //                    dropped only when its upper end is below the W-th largest
 //                    lower end seen.  What survives is rescored exactly, in
-//                    fp64 summed k = 0..R-1 (fp32 x fp32 products are exact in
-//                    fp64, so the sum is the oracle's bit for bit), and the
-//                    chunk's exact top-W is written out.
+//                    fp64 summed k = 0..R-1 over the fp32 E and F (fp32 x
+//                    fp32 products are exact in fp64, so the sum is the
+//                    oracle's bit for bit), and the chunk's exact top-W is
+//                    written out.
 //  frontier_kernel - one workgroup per request: merges the chunks' sorted
 //                    lists (the largest W-th entry of any list bounds the
 //                    frontier's W-th key from below, so only entries above it
@@ -39,6 +43,59 @@ namespace dt {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+
+// two floats rounded to bf16 (nearest, ties to even; finite inputs), packed
+// low element first
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    auto rne = [](float f) {
+        const uint32_t u = __float_as_uint(f);
+        return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    };
+    return rne(lo) | (rne(hi) << 16);
+}
+
+// one 16 x 16 tile of the screen's product on bf16 matrix cores: lane
+// (m, kq) holds KS consecutive features kq*KS .. kq*KS+KS-1 of its A row
+// (frontier node m) and B column (token m), two per word; the products are
+// exact in fp32 and accumulated in fp32
+template <int KS>
+__device__ __forceinline__ v4f mfma_bf16(const uint32_t (&a)[KS / 2], const uint32_t (&b)[KS / 2], v4f acc) {
+    if constexpr (KS == 4) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4v, u2v{a[0], a[1]}),
+                                                         __builtin_bit_cast(s4v, u2v{b[0], b[1]}), acc, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int h = 0; h < KS / 8; ++h)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf8v, u4v{a[4 * h], a[4 * h + 1], a[4 * h + 2], a[4 * h + 3]}),
+                __builtin_bit_cast(bf8v, u4v{b[4 * h], b[4 * h + 1], b[4 * h + 2], b[4 * h + 3]}), acc, 0, 0, 0);
+        return acc;
+    }
+}
+
+// lane (m, kq)'s KS bf16 features of token v's F row
+template <int KS>
+__device__ __forceinline__ void load_fbf(const uint16_t* __restrict__ Fbf, int64_t v, int kq, uint32_t (&f)[KS / 2]) {
+    const uint16_t* src = Fbf + v * (4 * KS) + kq * KS;
+    if constexpr (KS == 4) {
+        const uint2 q = *reinterpret_cast<const uint2*>(src);
+        f[0] = q.x;
+        f[1] = q.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < KS / 8; ++h) {
+            const uint4 q = reinterpret_cast<const uint4*>(src)[h];
+            f[4 * h] = q.x;
+            f[4 * h + 1] = q.y;
+            f[4 * h + 2] = q.z;
+            f[4 * h + 3] = q.w;
+        }
+    }
+}
 
 // raw logit bits (bf16 zero-extended, or fp32), widened only where used, so
 // that a prefetch is not waited for at the load
@@ -275,8 +332,9 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
     constexpr int R = 4 * KS;
     const int m = lane & 15, kq = lane >> 4;
 
-    // ---- the frontier rows of the wave's requests: A operands, Rk, |E_p|
+    // ---- the frontier rows of the wave's requests: A operands (bf16), Rk, |E_p|
     float A[kVocabReqPerWave][KS];
+    uint32_t Ab[kVocabReqPerWave][KS / 2];
     float eb[kVocabReqPerWave][4];
     int nf[kVocabReqPerWave], bq[kVocabReqPerWave];
 #pragma unroll
@@ -311,12 +369,18 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
         float ne = 0.f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) ne += A[j][s] * A[j][s];
+#pragma unroll
+        for (int s = 0; s < KS / 2; ++s) Ab[j][s] = bf16_pair(A[j][2 * s], A[j][2 * s + 1]);
         ne += __shfl_xor(ne, 16);
         ne += __shfl_xor(ne, 32);
+        // |g32 - g| <= (2 * 2^-8 + 2^-16) sum_k |E_k F_k| from rounding both
+        // operands to bf16, plus at most 2^-19 of it from the fp32
+        // accumulation, and sum_k |E_k F_k| <= |E_p| |F_v|: 2^-7 (1 + 2^-8)
+        // |E_p| |F_v| with room to spare at 1.125 * 2^-7
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * kq + i;
-            eb[j][i] = 0x1p-17f * sqrtf(__shfl(ne, r));
+            eb[j][i] = 0x1.2p-7f * sqrtf(__shfl(ne, r));
         }
     }
     __builtin_amdgcn_wave_barrier();
@@ -341,20 +405,13 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
     // scored; every load reads a valid address (the last column for the
     // padding of a ragged chunk) and validity is applied where the block is
     // used
-    float fc[KS], nc;
+    uint32_t fc[KS / 2];
+    float nc;
     uint32_t xc[kVocabReqPerWave];
     {
         const int v = col0 + (m < ncol ? m : ncol - 1);
         nc = a.fnorm[v];
-        const float4* fr = reinterpret_cast<const float4*>(a.F + (int64_t)v * R + kq * KS);
-#pragma unroll
-        for (int s4 = 0; s4 < KS / 4; ++s4) {
-            const float4 q = fr[s4];
-            fc[4 * s4 + 0] = q.x;
-            fc[4 * s4 + 1] = q.y;
-            fc[4 * s4 + 2] = q.z;
-            fc[4 * s4 + 3] = q.w;
-        }
+        load_fbf<KS>(a.Fbf, v, kq, fc);
 #pragma unroll
         for (int j = 0; j < kVocabReqPerWave; ++j) xc[j] = load_raw<DT>(a.logits, xrow[j] + v);
     }
@@ -362,21 +419,14 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
         const int cl = cb * 16 + m;
         const bool vv = cl < ncol;
         const int v = col0 + (vv ? cl : ncol - 1);
-        float fn[KS], nn = 0.f;
+        uint32_t fn[KS / 2];
+        float nn = 0.f;
         uint32_t xn[kVocabReqPerWave];
         if (cb + 1 < nblk) {                                            // wave-uniform
             const int cln = cl + 16;
             const int vn = col0 + (cln < ncol ? cln : ncol - 1);
             nn = a.fnorm[vn];
-            const float4* fr = reinterpret_cast<const float4*>(a.F + (int64_t)vn * R + kq * KS);
-#pragma unroll
-            for (int s4 = 0; s4 < KS / 4; ++s4) {
-                const float4 q = fr[s4];
-                fn[4 * s4 + 0] = q.x;
-                fn[4 * s4 + 1] = q.y;
-                fn[4 * s4 + 2] = q.z;
-                fn[4 * s4 + 3] = q.w;
-            }
+            load_fbf<KS>(a.Fbf, vn, kq, fn);
 #pragma unroll
             for (int j = 0; j < kVocabReqPerWave; ++j) xn[j] = load_raw<DT>(a.logits, xrow[j] + vn);
         }
@@ -385,11 +435,7 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
 #pragma unroll
         for (int j = 0; j < kVocabReqPerWave; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-#pragma unroll
-            for (int j = 0; j < kVocabReqPerWave; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[j][s], fc[s], acc[j], 0, 0, 0);
-        }
+        for (int j = 0; j < kVocabReqPerWave; ++j) acc[j] = mfma_bf16<KS>(Ab[j], fc, acc[j]);
 #pragma unroll
         for (int j = 0; j < kVocabReqPerWave; ++j) {
             if (nf[j] == 0) continue;                                   // wave-uniform
@@ -462,7 +508,7 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
         }
         if (cb + 1 < nblk) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) fc[s] = fn[s];
+            for (int s = 0; s < KS / 2; ++s) fc[s] = fn[s];
 #pragma unroll
             for (int j = 0; j < kVocabReqPerWave; ++j) xc[j] = xn[j];
             nc = nn;
@@ -924,28 +970,36 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
     }
 }
 
-// |F_v| for every token, once per call (the rounding bound of the screen)
+// |F_v| for every token (the rounding bound of the screen) and F rounded
+// to bf16 (the screen's matrix operand), once per call
+// (R/4 lanes per row, one 16-byte vector each, so a wave reads and writes
+// contiguous memory; the row's sum of squares is reduced across its lanes)
 template <int R>
-__global__ void __launch_bounds__(kThreads) fnorm_kernel(const float* __restrict__ F, int V, float* __restrict__ out) {
-    const int v = blockIdx.x * kThreads + threadIdx.x;
-    if (v >= V) return;
-    const float4* f4 = reinterpret_cast<const float4*>(F + (int64_t)v * R);
-    float s = 0.f;
+__global__ void __launch_bounds__(kThreads) fnorm_kernel(const float* __restrict__ F, int V, float* __restrict__ out,
+                                                         uint16_t* __restrict__ fbf) {
+    constexpr int LPR = R / 4;
+    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t v = gid / LPR;
+    const int sub = (int)(gid - v * LPR);
+    const bool in = v < V;
+    const float4 f = in ? reinterpret_cast<const float4*>(F + v * R)[sub] : make_float4(0.f, 0.f, 0.f, 0.f);
+    float s = f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
 #pragma unroll
-    for (int q = 0; q < R / 4; ++q) {
-        const float4 f = f4[q];
-        s += f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
+    for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
+    if (in) {
+        reinterpret_cast<uint2*>(fbf + v * R)[sub] = make_uint2(bf16_pair(f.x, f.y), bf16_pair(f.z, f.w));
+        if (sub == 0) out[v] = sqrtf(s) * (1.f + 0x1p-20f);
     }
-    out[v] = sqrtf(s) * (1.f + 0x1p-20f);
 }
 
 }  // namespace
 
-hipError_t launch_fnorm(const float* F, int V, int R, float* out, hipStream_t stream) {
-    const dim3 grid((unsigned)((V + kThreads - 1) / kThreads)), block(kThreads);
-    if (R == 16) hipLaunchKernelGGL(fnorm_kernel<16>, grid, block, 0, stream, F, V, out);
-    else if (R == 32) hipLaunchKernelGGL(fnorm_kernel<32>, grid, block, 0, stream, F, V, out);
-    else if (R == 64) hipLaunchKernelGGL(fnorm_kernel<64>, grid, block, 0, stream, F, V, out);
+hipError_t launch_fnorm(const float* F, int V, int R, float* out, uint16_t* fbf, hipStream_t stream) {
+    const int64_t threads = (int64_t)V * (R / 4);
+    const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
+    if (R == 16) hipLaunchKernelGGL(fnorm_kernel<16>, grid, block, 0, stream, F, V, out, fbf);
+    else if (R == 32) hipLaunchKernelGGL(fnorm_kernel<32>, grid, block, 0, stream, F, V, out, fbf);
+    else if (R == 64) hipLaunchKernelGGL(fnorm_kernel<64>, grid, block, 0, stream, F, V, out, fbf);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -49,7 +49,7 @@
  * proposals, ranked as in step 3.  This equals the top-W over every
  * (node, token) pair.  k is not used for proposals; the N-gram table must
  * be of kind NONE; W <= 16 and R in {16, 32, 64}.  Keys are exact fp64 (the
- * dense product runs on fp32 matrix cores only to discard tokens that
+ * dense product runs on bf16 matrix cores only to discard tokens that
  * provably cannot be selected).  Best-first selection is replayed literally
  * (g may be positive, so S can rise along a path).
  *
@@ -186,12 +186,13 @@ dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngram,
 
 /* Bytes of workspace dt_build_tree / dt_position_topk need for these
  * parameters (depends on B, V, d, k, mode, dtype and sweep_chunks only, and
- * on W in DARTREE_FULL mode; the N-gram area is sized for the largest table
- * kind); 0 if the parameters are invalid.  The workspace holds the sweep's
- * per-chunk partials and the per-row normalisers, top-k lists, continuity
- * masks (and DARTree terms) the tree step reads; in DARTREE_FULL mode also
- * the frontier, the candidate tree and every vocabulary chunk's top-W.  Its
- * contents are meaningless between calls. */
+ * on W and R in DARTREE_FULL mode; the N-gram area is sized for the largest
+ * table kind); 0 if the parameters are invalid.  The workspace holds the
+ * sweep's per-chunk partials and the per-row normalisers, top-k lists,
+ * continuity masks (and DARTree terms) the tree step reads; in DARTREE_FULL
+ * mode also the frontier, the candidate tree, the column norms and a bf16
+ * copy of F (V * R * 2 bytes) for the matrix-core screen, and every
+ * vocabulary chunk's top-W.  Its contents are meaningless between calls. */
 size_t dt_workspace_size(const dt_params* params);
 
 /* Static, human-readable name of a status code. */
