@@ -419,17 +419,17 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
         const int cl = cb * 16 + m;
         const bool vv = cl < ncol;
         const int v = col0 + (vv ? cl : ncol - 1);
+        // the next block's loads are issued on every iteration (the last one
+        // re-reads the chunk's last column): a conditional load would make
+        // the compiler wait for them before this block's products
         uint32_t fn[KS / 2];
-        float nn = 0.f;
         uint32_t xn[kVocabReqPerWave];
-        if (cb + 1 < nblk) {                                            // wave-uniform
-            const int cln = cl + 16;
-            const int vn = col0 + (cln < ncol ? cln : ncol - 1);
-            nn = a.fnorm[vn];
-            load_fbf<KS>(a.Fbf, vn, kq, fn);
+        const int cln = cl + 16;
+        const int vn = col0 + (cln < ncol ? cln : ncol - 1);
+        const float nn = a.fnorm[vn];
+        load_fbf<KS>(a.Fbf, vn, kq, fn);
 #pragma unroll
-            for (int j = 0; j < kVocabReqPerWave; ++j) xn[j] = load_raw<DT>(a.logits, xrow[j] + vn);
-        }
+        for (int j = 0; j < kVocabReqPerWave; ++j) xn[j] = load_raw<DT>(a.logits, xrow[j] + vn);
         const float nfv = nc;
         v4f acc[kVocabReqPerWave];
 #pragma unroll
@@ -506,13 +506,11 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
             }
             row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq]);
         }
-        if (cb + 1 < nblk) {
 #pragma unroll
-            for (int s = 0; s < KS / 2; ++s) fc[s] = fn[s];
+        for (int s = 0; s < KS / 2; ++s) fc[s] = fn[s];
 #pragma unroll
-            for (int j = 0; j < kVocabReqPerWave; ++j) xc[j] = xn[j];
-            nc = nn;
-        }
+        for (int j = 0; j < kVocabReqPerWave; ++j) xc[j] = xn[j];
+        nc = nn;
     }
 
     // ---- the chunk's exact top-W per request
