@@ -738,22 +738,76 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     // ---- load what the prep kernel derived for this request (contiguous)
     {
         const int64_t r0 = (int64_t)b * d;
-        for (int i = tid; i < d; i += kTreeThreads) s_lse[i] = a.lse[r0 + i];
-        for (int i = tid; i < d * k; i += kTreeThreads) {
+        const int dk = d * k, nc = P.n_ctx;
+        // The first round of every array (up to four entries per thread:
+        // all of them at the usual sizes) is loaded before anything is
+        // stored, so the loads share one memory round trip; the indices are
+        // clamped so that every load is issued unconditionally.
+        constexpr int U4 = 4;
+        const double l_lse = a.lse[r0 + (tid < d ? tid : 0)];
+        int l_tok[U4];
+        float l_tx[U4];
+        uint32_t l_vm[U4];
+#pragma unroll
+        for (int u = 0; u < U4; ++u) {
+            const int i = tid + u * kTreeThreads, ic = i < dk ? i : 0;
+            l_tok[u] = a.ttok[r0 * k + ic];
+            l_tx[u] = a.tx[r0 * k + ic];
+        }
+        if (nc > 0) {
+#pragma unroll
+            for (int u = 0; u < U4; ++u) {
+                const int i = tid + u * kTreeThreads, ic = i < nc ? i : 0;
+                l_vm[u] = a.vmask[(int64_t)b * a.n_ctx + ic];
+            }
+        }
+        typedef double d2 __attribute__((ext_vector_type(2)));
+        const double* gsrc = a.g + r0 * k * k;
+        const int ng = dartree ? d * k * k : 0;
+        const bool gvec = (((uintptr_t)gsrc | (uintptr_t)s_g) & 15u) == 0 && (ng & 1) == 0;
+        const int nv = ng >> 1;
+        constexpr int UG = 8;
+        d2 l_g[UG];
+        if (dartree && gvec) {
+            const d2* src = reinterpret_cast<const d2*>(gsrc);
+#pragma unroll
+            for (int u = 0; u < UG; ++u) {
+                const int i = tid + u * kTreeThreads;
+                l_g[u] = src[i < nv ? i : 0];
+            }
+        }
+        if (tid < d) s_lse[tid] = l_lse;
+#pragma unroll
+        for (int u = 0; u < U4; ++u) {
+            const int i = tid + u * kTreeThreads;
+            if (i < dk) {
+                s_ttok[i] = l_tok[u];
+                s_tx[i] = l_tx[u];
+            }
+        }
+        if (nc > 0) {
+#pragma unroll
+            for (int u = 0; u < U4; ++u) {
+                const int i = tid + u * kTreeThreads;
+                if (i < nc) s_vmask[i] = l_vm[u];
+            }
+        }
+        // the rest, rarely any (d < 256 always)
+        for (int i = tid + U4 * kTreeThreads; i < dk; i += kTreeThreads) {
             s_ttok[i] = a.ttok[r0 * k + i];
             s_tx[i] = a.tx[r0 * k + i];
         }
-        for (int i = tid; i < P.n_ctx; i += kTreeThreads) s_vmask[i] = a.vmask[(int64_t)b * a.n_ctx + i];
+        for (int i = tid + U4 * kTreeThreads; i < nc; i += kTreeThreads) s_vmask[i] = a.vmask[(int64_t)b * a.n_ctx + i];
         if (dartree) {
-            const double* gsrc = a.g + r0 * k * k;
-            const int ng = d * k * k;
-            if ((((uintptr_t)gsrc | (uintptr_t)s_g) & 15u) == 0 && (ng & 1) == 0) {
-                // 16-byte vectors, four in flight per thread before the stores
-                typedef double d2 __attribute__((ext_vector_type(2)));
+            if (gvec) {
                 const d2* src = reinterpret_cast<const d2*>(gsrc);
                 d2* dst = reinterpret_cast<d2*>(s_g);
-                const int nv = ng >> 1;
-                for (int base = 0; base < nv; base += 4 * kTreeThreads) {
+#pragma unroll
+                for (int u = 0; u < UG; ++u) {
+                    const int i = tid + u * kTreeThreads;
+                    if (i < nv) dst[i] = l_g[u];
+                }
+                for (int base = UG * kTreeThreads; base < nv; base += 4 * kTreeThreads) {
                     d2 v0, v1, v2, v3;
                     const int i0 = base + tid, i1 = i0 + kTreeThreads, i2 = i1 + kTreeThreads, i3 = i2 + kTreeThreads;
                     if (i0 < nv) v0 = src[i0];
