@@ -390,7 +390,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures the single-GPU path only; --gpus must be 1 "
-              "(requests shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(requests shard across GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
     if args.traffic_from:
         r = "$R/" + os.path.relpath(args.traffic_from, ROOT)

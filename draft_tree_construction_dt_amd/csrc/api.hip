@@ -187,7 +187,7 @@ extern "C" const char* dt_status_string(dt_status s) {
     switch (s) {
     case DT_OK: return "DT_OK";
     case DT_ERR_INVALID_ARG: return "DT_ERR_INVALID_ARG: null pointer, value out of range or misaligned buffer";
-    case DT_ERR_UNSUPPORTED: return "DT_ERR_UNSUPPORTED: outside the limits of this build";
+    case DT_ERR_UNSUPPORTED: return "DT_ERR_UNSUPPORTED: outside the library's limits";
     case DT_ERR_WORKSPACE: return "DT_ERR_WORKSPACE: workspace missing, misaligned or smaller than dt_workspace_size()";
     case DT_ERR_HIP: return "DT_ERR_HIP: the HIP runtime refused a launch";
     default: return "unknown dt_status";

@@ -103,7 +103,7 @@ extern "C" {
 typedef enum dt_status {
     DT_OK = 0,
     DT_ERR_INVALID_ARG = 1,   /* a null pointer, a value out of range, a misaligned buffer */
-    DT_ERR_UNSUPPORTED = 2,   /* valid but outside this build's limits (see above) */
+    DT_ERR_UNSUPPORTED = 2,   /* valid but outside the library's limits (see above) */
     DT_ERR_WORKSPACE = 3,     /* workspace missing or smaller than dt_workspace_size() */
     DT_ERR_HIP = 4            /* the HIP runtime refused a launch */
 } dt_status;

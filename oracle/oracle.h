@@ -16,7 +16,7 @@
  *    the top-W across the whole frontier kept after every depth, then
  *    best-first pruning selects the verification tree.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *  - the N-gram is a hard filter, keep iff logp > min_logp (strict); with
  *    min_logp = -INFINITY sparse tables test membership only;
  *  - continuity is checked at every depth, depth 1 against the committed

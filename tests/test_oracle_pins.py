@@ -1,6 +1,6 @@
 """Pins of the CPU oracle against things other than itself.
 
-Each test names what it pins (P1..P7 in the design doc's parity table).  None of
+Each test names what it pins (pins P1..P7).  None of
 them calls the HIP library.
 """
 
