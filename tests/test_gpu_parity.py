@@ -240,6 +240,51 @@ def test_tight_bound_many_candidates(device, oracle_lib):
         _parity(p, device, oracle_lib, label=f"many candidates mode={mode} W={W} k={k}")
 
 
+def test_random_campaign(device, oracle_lib):
+    """Four hundred random problems over every mode, table kind, dtype and
+    launch plan (V up to 5000, k up to 32, W up to 64, d up to 10, budgets
+    from 1 past d*W, integer logits for exact ties, -inf logits, strong
+    parent terms).  Parameters outside the library's limits must be refused
+    with DT_ERR_UNSUPPORTED; every other problem must match the oracle."""
+    from draft_tree_construction_dt_amd import binding as bd
+    from refcheck import MODE_DARTREE_FULL
+    rng = np.random.default_rng(2024)
+    refused = 0
+    for n in range(400):
+        mode = [MODE_DART, MODE_DART, MODE_DARTREE, MODE_DARTREE_FULL][int(rng.integers(0, 4))]
+        kind = NGRAM_NONE if mode == MODE_DARTREE_FULL else int(rng.choice(KINDS))
+        vmax = {NGRAM_HASH_TRIGRAM: 250, NGRAM_DENSE_BIGRAM: 1500}.get(kind, 5000)
+        V = int(rng.integers(2, vmax))
+        if mode == MODE_DARTREE_FULL:
+            W = int(rng.integers(1, 17))
+            k = min(W, V)
+            R = int(rng.choice([16, 32, 64]))
+        else:
+            k = int(rng.integers(1, min(V, 32) + 1))
+            W = int(rng.integers(1, min(64, 1024 // k) + 1))
+            R = int(rng.choice([4, 8, 16, 64]))
+        d = int(rng.integers(1, 11))
+        budget = min(int(rng.integers(1, d * W + 3)), 1024)
+        p = synth.random_problem(
+            rng, B=int(rng.integers(1, 7)), V=V, d=d, k=k, W=W, budget=budget, ngram=kind, mode=mode,
+            dtype=synth.DTYPE_BF16 if rng.random() < 0.5 else synth.DTYPE_F32,
+            density=float(rng.uniform(0.05, 0.9)),
+            min_logp=-1.0 if (kind != NGRAM_NONE and rng.random() < 0.3) else -math.inf,
+            hash_cap=int(2 ** rng.integers(4, 12)), hash_S=int(rng.integers(1, 20)),
+            csr_deg=int(rng.integers(1, 40)), neg_inf_frac=0.05 if rng.random() < 0.2 else 0.0,
+            integer_logits=bool(rng.random() < 0.15), R=R, sigma=float(rng.choice([0.5, 2.0, 6.0])))
+        if mode == MODE_DARTREE and rng.random() < 0.3:
+            p.E *= 4
+        chunks = int(rng.integers(0, 5)) if mode != MODE_DARTREE_FULL else 0
+        try:
+            _parity(p, device, oracle_lib, sweep_chunks=chunks, label=f"campaign {n} mode={mode} kind={kind}")
+        except bd.DtError as e:
+            assert e.status == bd.DT_ERR_UNSUPPORTED, str(e)
+            refused += 1
+    _say(f"[campaign] {400 - refused} problems matched, {refused} refused as unsupported")
+    assert refused < 60
+
+
 def test_zero_requests(device):
     import torch
     from draft_tree_construction_dt_amd import binding as bd
