@@ -22,7 +22,7 @@ constexpr int kTreeWaves = kTreeThreads / 64;
 constexpr int kPrepRows = 3;           // rows a prep workgroup merges: children, parents, grandparents
 constexpr int kPrepContexts = 64;      // trigram contexts per prep workgroup (one per lane quad)
 constexpr int kMiscInts = 32;          // tree-kernel counters (0..3) and scan scratch (16..31)
-constexpr int kTreeLdsLimit = 64 * 1024;
+constexpr int kTreeLdsLimit = 160 * 1024;
 constexpr int kMergeKeysPerRow = 256;  // C * 4 * k bound: per-wave merge scratch
 constexpr int kSweepVecsPerThread = 4; // 16-byte vectors each thread holds per batch
 constexpr int kSweepCap = 128;         // per-wave candidate buffer of the sweep

@@ -86,7 +86,8 @@
  *     W * k <= 1024; 1 <= budget <= 1024; 1 <= V < 2^26; the logits
  *     pointer 16-byte aligned; and the tree kernel's shared-memory plan
  *     (which grows with d, k, W, the N-gram kind and the mode) must fit in
- *     64 KiB, else DT_ERR_UNSUPPORTED.  DARTREE mode needs E and F 16-byte
+ *     the 160 KiB of LDS a gfx950 workgroup may use, else
+ *     DT_ERR_UNSUPPORTED.  DARTREE mode needs E and F 16-byte
  *     aligned with R a multiple of 4, 4 <= R <= 256.  A trigram table's
  *     keys array must be 16-byte aligned.
  */

@@ -240,6 +240,22 @@ def test_tight_bound_many_candidates(device, oracle_lib):
         _parity(p, device, oracle_lib, label=f"many candidates mode={mode} W={W} k={k}")
 
 
+def test_large_shared_plans(device, oracle_lib):
+    """Tree-kernel shared-memory plans between 64 and 160 KiB: many
+    candidates per depth with long trees, a wide trigram context table, and
+    DARTree terms for deep trees."""
+    rng = np.random.default_rng(61)
+    cases = [
+        dict(B=4, V=694, d=10, k=16, W=57, budget=427, ngram=NGRAM_NONE, mode=MODE_DART),
+        dict(B=3, V=114, d=10, k=28, W=32, budget=222, ngram=NGRAM_HASH_TRIGRAM, mode=MODE_DART,
+             hash_cap=1024, hash_S=12, density=0.5),
+        dict(B=3, V=427, d=9, k=22, W=42, budget=268, ngram=NGRAM_NONE, mode=MODE_DARTREE, R=16),
+    ]
+    for i, c in enumerate(cases):
+        p = synth.random_problem(rng, dtype=synth.DTYPE_BF16 if i % 2 else synth.DTYPE_F32, **c)
+        _parity(p, device, oracle_lib, label=f"large plan {i}")
+
+
 def test_random_campaign(device, oracle_lib):
     """Four hundred random problems over every mode, table kind, dtype and
     launch plan (V up to 5000, k up to 32, W up to 64, d up to 10, budgets
