@@ -730,14 +730,22 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
             nq += __popcll(mq);
         }
         __syncthreads();
-        if (lane == 0) {
-            int o = 0;
-            for (int i = 0; i < nq; ++i) {
-                s_off[i] = o;
-                o += s_q[i] >> 16;
+        // offsets of the lists' entries: an exclusive scan of their lengths,
+        // 64 lists per round
+        int run = 0;
+        for (int i0 = 0; i0 < nq; i0 += 64) {
+            const int i = i0 + lane;
+            const int len = i < nq ? s_q[i] >> 16 : 0;
+            int x = len;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o);
+                if (lane >= o) x += y;
             }
-            s_off[nq] = o;
+            if (i < nq) s_off[i] = run + x - len;
+            run += __shfl(x, 63);
         }
+        if (lane == 0) s_off[nq] = run;
         __syncthreads();
         for (int it = lane; it < total; it += 64) {
             int lo = 0, hi = nq - 1;                                    // the list holding item it
