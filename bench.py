@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--sets", type=int, default=5, help="distinct B=64 input sets to rotate over")
     ap.add_argument("--b1-steps", type=int, default=2000, help="timed single-request calls")
-    ap.add_argument("--cpu-sample", type=int, default=64, help="requests the oracle builds for cpu_baseline")
+    ap.add_argument("--cpu-sample", type=int, default=128,
+                    help="requests the oracle builds for cpu_baseline (about 12 s of one core)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--streams", type=int, default=4,
                     help="HIP streams the calls alternate over (consecutive batches in flight together)")
@@ -624,7 +625,7 @@ def main():
 
     if not args.no_cpu:
         import oracle
-        n = min(args.cpu_sample, BATCH)
+        n = max(1, min(args.cpu_sample, prob.B))
         sample = copy.copy(prob)
         sample.B = n
         sample.logits = prob.logits[:n]
@@ -637,7 +638,7 @@ def main():
             "unit": "trees/s",
             "cores": 1,
             "kind": "oracle",
-            "sample": f"the first {n} requests of input set 0 (whole path: normaliser, top-k, "
+            "sample": f"the first {n} requests of the input sets, {-(-n // BATCH)} batch(es) of {BATCH} (whole path: normaliser, top-k, "
                       f"trigram expansion, top-W, budget, mask), single-threaded C, {cpu_s:.1f}s",
         }
     print(json.dumps(res), flush=True)
