@@ -88,7 +88,8 @@ def _call(params, ngram=None, logits=FAKE, out=None, workspace=True):
     (dict(sweep_chunks=200, k=5), bd.DT_ERR_UNSUPPORTED),
     (dict(mode=bd.DT_MODE_DARTREE), bd.DT_ERR_INVALID_ARG),             # E, F missing
     (dict(mode=bd.DT_MODE_DARTREE, E=FAKE, F=FAKE, R=6), bd.DT_ERR_UNSUPPORTED),
-    (dict(d=32, W=64, k=16), bd.DT_ERR_UNSUPPORTED),                    # shared-memory plan too big
+    (dict(mode=bd.DT_MODE_DARTREE, E=FAKE, F=FAKE, R=8, d=32, W=32, k=32),
+     bd.DT_ERR_UNSUPPORTED),                                             # shared-memory plan over 160 KiB
 ])
 def test_invalid_parameters(kw, status):
     assert _call(_params(**kw)) == status
