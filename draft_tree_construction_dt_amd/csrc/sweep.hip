@@ -10,8 +10,10 @@
 // barriers, no shared state between waves).  Each thread
 // keeps kSweepVecsPerThread 16-byte vectors (8 bf16 or 4 fp32) per batch, the
 // 64 lanes of a wave reading 1 KiB contiguous per load; loads are
-// non-temporal (streamed once) and the next batch is loaded before the
-// current one is reduced.  Per lane: online max and sum in the exp2 domain
+// non-temporal (streamed once) and the next batch is loaded into the other
+// of two register sets before the current one is reduced (no copies, and no
+// branch around the loads, so the compiler waits only for the batch it
+// needs).  Per lane: online max and sum in the exp2 domain
 // (v_exp_f32), batch sums in fp32 folded into an fp64 accumulator.  Per
 // wave: an exact top-k by threshold filtering -- an element enters the
 // wave's LDS buffer only if its key beats the current k-th key -- with the
@@ -214,14 +216,37 @@ __device__ __forceinline__ void unpack(const vec4& r, float* out) {
     }
 }
 
+// Unguarded loads: a vector past the chunk's end reads the chunk's last
+// vector instead (a valid address; the batch that holds it masks it out), so
+// every load is issued and the compiler can count the loads in flight.
 template <bool BF16>
-__device__ __forceinline__ void load_batch(vec4 (&r)[U], const vec4* vbase, int64_t q, int64_t v_hi) {
-    constexpr uint32_t NEG = BF16 ? 0xFF80FF80u : 0xFF800000u;   // -inf patterns
+__device__ __forceinline__ void load_clamped(vec4 (&r)[U], const vec4* vbase, int64_t q, int64_t v_hi) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t qu = q + (int64_t)u * kThreads;
-        r[u] = qu < v_hi ? __builtin_nontemporal_load(vbase + qu) : vec4{NEG, NEG, NEG, NEG};
+        r[u] = __builtin_nontemporal_load(vbase + (qu < v_hi ? qu : v_hi - 1));
     }
+}
+
+// One batch of vectors q0 + u * kThreads: vectors past the chunk's end (only
+// in a partial last batch) become -inf, then the batch is folded in.
+template <bool BF16, int NE, int EPV>
+__device__ __forceinline__ void eat_batch(vec4 (&r)[U], int64_t q0, int64_t v_hi, bool partial, int64_t row0,
+                                          WaveState& st, unsigned long long* buf, float* stage, float* seeds,
+                                          int k, int trig, int lane, int wave) {
+    constexpr uint32_t NEG = BF16 ? 0xFF80FF80u : 0xFF800000u;   // -inf patterns
+    bool vok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) vok[u] = q0 + (int64_t)u * kThreads < v_hi;
+    if (partial) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (!vok[u]) r[u] = vec4{NEG, NEG, NEG, NEG};
+    }
+    float xs[NE];
+#pragma unroll
+    for (int u = 0; u < U; ++u) unpack<BF16>(r[u], xs + u * EPV);
+    consume<NE, EPV>(xs, (int)(q0 * EPV - row0), kThreads * EPV, vok, st, buf, stage, seeds, k, trig, lane, wave);
 }
 
 template <bool BF16>
@@ -267,31 +292,35 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
     st.thid = 0xFFFFFFFFu;
     st.fresh = true;
 
-    // ---- batches of kThreads*U vectors, software pipelined: the next batch
-    //      (the last one guarded) is loaded before the current one is reduced
+    // ---- batches of kThreads*U vectors, software pipelined over two
+    //      register sets: the next batch is loaded before the current one is
+    //      reduced, with no copies between the sets and every load issued
+    //      unconditionally in the steady state (only the last batch can be
+    //      partial)
     const int64_t per_batch = (int64_t)kThreads * U;
     const int64_t nvec = v_hi - v_lo;
     const int64_t nbat = (nvec + per_batch - 1) / per_batch;
     if (nbat > 0) {
-        vec4 cur[U];
-        load_batch<BF16>(cur, vbase, v_lo + tid, v_hi);
-        for (int64_t bi = 0; bi < nbat; ++bi) {
+        vec4 ra[U], rb[U];
+        load_clamped<BF16>(ra, vbase, v_lo + tid, v_hi);
+        int64_t bi = 0;
+        for (; bi + 2 < nbat; bi += 2) {                 // batches bi and bi+1 are full
             const int64_t q0 = v_lo + bi * per_batch + tid;
-            vec4 nxt[U];
-            if (bi + 1 < nbat) load_batch<BF16>(nxt, vbase, q0 + per_batch, v_hi);
-            float xs[NE];
-            bool vok[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                unpack<BF16>(cur[u], xs + u * EPV);
-                vok[u] = q0 + (int64_t)u * kThreads < v_hi;
-            }
-            consume<NE, EPV>(xs, (int)(q0 * EPV - row0), kThreads * EPV, vok, st, buf, stage, s_seeds, k, trig, lane,
-                             wave);
-            if (bi + 1 < nbat) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-            }
+            load_clamped<BF16>(rb, vbase, q0 + per_batch, v_hi);
+            eat_batch<BF16, NE, EPV>(ra, q0, v_hi, false, row0, st, buf, stage, s_seeds, k, trig, lane, wave);
+            load_clamped<BF16>(ra, vbase, q0 + 2 * per_batch, v_hi);
+            eat_batch<BF16, NE, EPV>(rb, q0 + per_batch, v_hi, false, row0, st, buf, stage, s_seeds, k, trig, lane,
+                                     wave);
+        }
+        const int64_t q0 = v_lo + bi * per_batch + tid;
+        if (bi + 1 < nbat) {                             // two left: bi full, bi+1 the last
+            load_clamped<BF16>(rb, vbase, q0 + per_batch, v_hi);
+            eat_batch<BF16, NE, EPV>(ra, q0, v_hi, false, row0, st, buf, stage, s_seeds, k, trig, lane, wave);
+            eat_batch<BF16, NE, EPV>(rb, q0 + per_batch, v_hi, (bi + 2) * per_batch > nvec, row0, st, buf, stage,
+                                     s_seeds, k, trig, lane, wave);
+        } else {                                         // one left: the last
+            eat_batch<BF16, NE, EPV>(ra, q0, v_hi, (bi + 1) * per_batch > nvec, row0, st, buf, stage, s_seeds, k,
+                                     trig, lane, wave);
         }
     }
     // ---- elements outside the aligned vectors (row ends that are not 16-byte aligned)
