@@ -229,16 +229,17 @@ __device__ __forceinline__ void load_clamped(vec4 (&r)[U], const vec4* vbase, in
 }
 
 // One batch of vectors q0 + u * kThreads: vectors past the chunk's end (only
-// in a partial last batch) become -inf, then the batch is folded in.
-template <bool BF16, int NE, int EPV>
+// in a partial last batch) become -inf, then the batch is folded in.  FULL:
+// the batch is known to lie inside the chunk.
+template <bool BF16, int NE, int EPV, bool FULL>
 __device__ __forceinline__ void eat_batch(vec4 (&r)[U], int64_t q0, int64_t v_hi, bool partial, int64_t row0,
                                           WaveState& st, unsigned long long* buf, float* stage, float* seeds,
                                           int k, int trig, int lane, int wave) {
     constexpr uint32_t NEG = BF16 ? 0xFF80FF80u : 0xFF800000u;   // -inf patterns
     bool vok[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) vok[u] = q0 + (int64_t)u * kThreads < v_hi;
-    if (partial) {
+    for (int u = 0; u < U; ++u) vok[u] = FULL || q0 + (int64_t)u * kThreads < v_hi;
+    if (!FULL && partial) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (!vok[u]) r[u] = vec4{NEG, NEG, NEG, NEG};
@@ -307,20 +308,20 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
         for (; bi + 2 < nbat; bi += 2) {                 // batches bi and bi+1 are full
             const int64_t q0 = v_lo + bi * per_batch + tid;
             load_clamped<BF16>(rb, vbase, q0 + per_batch, v_hi);
-            eat_batch<BF16, NE, EPV>(ra, q0, v_hi, false, row0, st, buf, stage, s_seeds, k, trig, lane, wave);
+            eat_batch<BF16, NE, EPV, true>(ra, q0, v_hi, false, row0, st, buf, stage, s_seeds, k, trig, lane, wave);
             load_clamped<BF16>(ra, vbase, q0 + 2 * per_batch, v_hi);
-            eat_batch<BF16, NE, EPV>(rb, q0 + per_batch, v_hi, false, row0, st, buf, stage, s_seeds, k, trig, lane,
-                                     wave);
+            eat_batch<BF16, NE, EPV, true>(rb, q0 + per_batch, v_hi, false, row0, st, buf, stage, s_seeds, k, trig,
+                                           lane, wave);
         }
         const int64_t q0 = v_lo + bi * per_batch + tid;
         if (bi + 1 < nbat) {                             // two left: bi full, bi+1 the last
             load_clamped<BF16>(rb, vbase, q0 + per_batch, v_hi);
-            eat_batch<BF16, NE, EPV>(ra, q0, v_hi, false, row0, st, buf, stage, s_seeds, k, trig, lane, wave);
-            eat_batch<BF16, NE, EPV>(rb, q0 + per_batch, v_hi, (bi + 2) * per_batch > nvec, row0, st, buf, stage,
-                                     s_seeds, k, trig, lane, wave);
+            eat_batch<BF16, NE, EPV, true>(ra, q0, v_hi, false, row0, st, buf, stage, s_seeds, k, trig, lane, wave);
+            eat_batch<BF16, NE, EPV, false>(rb, q0 + per_batch, v_hi, (bi + 2) * per_batch > nvec, row0, st, buf,
+                                            stage, s_seeds, k, trig, lane, wave);
         } else {                                         // one left: the last
-            eat_batch<BF16, NE, EPV>(ra, q0, v_hi, (bi + 1) * per_batch > nvec, row0, st, buf, stage, s_seeds, k,
-                                     trig, lane, wave);
+            eat_batch<BF16, NE, EPV, false>(ra, q0, v_hi, (bi + 1) * per_batch > nvec, row0, st, buf, stage, s_seeds,
+                                            k, trig, lane, wave);
         }
     }
     // ---- elements outside the aligned vectors (row ends that are not 16-byte aligned)
