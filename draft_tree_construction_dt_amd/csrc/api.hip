@@ -166,7 +166,9 @@ static dt_status check_ngram(const dt_ngram_table* g) {
     case DT_NGRAM_DENSE_BIGRAM:
         return g->dense_logp ? DT_OK : DT_ERR_INVALID_ARG;
     case DT_NGRAM_CSR_BIGRAM:
-        if (!g->row_ptr || !g->col || (finite && !g->csr_logp)) return DT_ERR_INVALID_ARG;
+        // an empty table (nnz = 0) needs no successor arrays
+        if (!g->row_ptr || g->nnz < 0) return DT_ERR_INVALID_ARG;
+        if (g->nnz > 0 && (!g->col || (finite && !g->csr_logp))) return DT_ERR_INVALID_ARG;
         return DT_OK;
     case DT_NGRAM_HASH_TRIGRAM:
         if (!g->keys || !g->succ || (finite && !g->hash_logp)) return DT_ERR_INVALID_ARG;

@@ -127,7 +127,8 @@ typedef enum dt_ngram_kind {
 /* N-gram continuity table (device arrays; unused fields may be NULL).
  *  dense:  dense_logp[V][V] float.
  *  CSR:    row_ptr[V+1] int32, col[nnz] int32 ascending within a row,
- *          csr_logp[nnz] float (may be NULL when min_logp = -INFINITY).
+ *          csr_logp[nnz] float (may be NULL when min_logp = -INFINITY);
+ *          col and csr_logp may be NULL when nnz = 0 (every row empty).
  *  hash:   keys[cap] uint64 with key = (uint64)t_-2 << 32 | (uint32)t_-1 and
  *          0xFFFFFFFFFFFFFFFF marking a free slot; a key lives in the first
  *          free slot at or after splitmix64(key) & (cap - 1) (the SplitMix64

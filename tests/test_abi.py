@@ -95,12 +95,26 @@ def test_invalid_parameters(kw, status):
     assert _call(_params(**kw)) == status
 
 
+class _Csr:
+    """A CSR table descriptor with explicit pointers and entry count."""
+
+    def __init__(self, row_ptr, col, nnz, min_logp=-math.inf):
+        self.row_ptr, self.col, self.nnz, self.min_logp = row_ptr, col, nnz, min_logp
+
+    def _c(self):
+        g = bd.NGram(kind=bd.DT_NGRAM_CSR_BIGRAM, min_logp=self.min_logp)._c()
+        g.row_ptr, g.col, g.nnz = self.row_ptr or None, self.col or None, self.nnz
+        return g
+
+
 def test_invalid_tables_and_buffers():
     P = _params()
     assert _call(P, bd.NGram(kind=9)) == bd.DT_ERR_INVALID_ARG
     assert _call(P, bd.NGram(kind=bd.DT_NGRAM_DENSE_BIGRAM)) == bd.DT_ERR_INVALID_ARG
-    assert _call(P, bd.NGram(kind=bd.DT_NGRAM_CSR_BIGRAM, row_ptr=FAKE)) == bd.DT_ERR_INVALID_ARG
-    assert _call(P, bd.NGram(kind=bd.DT_NGRAM_CSR_BIGRAM, row_ptr=FAKE, col=FAKE, min_logp=-2.0)) == \
+    assert _call(P, _Csr(row_ptr=0, col=FAKE, nnz=5)) == bd.DT_ERR_INVALID_ARG
+    assert _call(P, _Csr(row_ptr=FAKE, col=0, nnz=5)) == bd.DT_ERR_INVALID_ARG        # entries, no array
+    assert _call(P, _Csr(row_ptr=FAKE, col=FAKE, nnz=-1)) == bd.DT_ERR_INVALID_ARG
+    assert _call(P, _Csr(row_ptr=FAKE, col=FAKE, nnz=5, min_logp=-2.0)) == \
         bd.DT_ERR_INVALID_ARG                                            # finite threshold needs logp
     hk = dict(kind=bd.DT_NGRAM_HASH_TRIGRAM, keys=FAKE, succ=FAKE, S=16)
     assert _call(P, bd.NGram(cap=1000, **hk)) == bd.DT_ERR_INVALID_ARG      # not a power of two

@@ -240,6 +240,18 @@ def test_tight_bound_many_candidates(device, oracle_lib):
         _parity(p, device, oracle_lib, label=f"many candidates mode={mode} W={W} k={k}")
 
 
+def test_empty_csr_table(device, oracle_lib):
+    """A CSR table with no successors at all (nnz = 0, no successor arrays):
+    nothing is admitted."""
+    rng = np.random.default_rng(71)
+    p = synth.random_problem(rng, B=2, V=40, d=4, k=4, W=4, budget=16, ngram=NGRAM_CSR_BIGRAM, csr_deg=1)
+    p.ngram.row_ptr[:] = 0
+    p.ngram.col = np.zeros(0, dtype=np.int32)
+    p.ngram.csr_logp = np.zeros(0, dtype=np.float32)
+    gpu, _ = _parity(p, device, oracle_lib, label="empty csr")
+    assert np.all(gpu["n_nodes"] == 0)
+
+
 def test_large_shared_plans(device, oracle_lib):
     """Tree-kernel shared-memory plans between 64 and 160 KiB: many
     candidates per depth with long trees, a wide trigram context table, and
