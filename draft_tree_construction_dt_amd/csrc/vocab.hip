@@ -374,9 +374,10 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
         ne += __shfl_xor(ne, 16);
         ne += __shfl_xor(ne, 32);
         // |g32 - g| <= (2 * 2^-8 + 2^-16) sum_k |E_k F_k| from rounding both
-        // operands to bf16, plus at most 2^-19 of it from the fp32
-        // accumulation, and sum_k |E_k F_k| <= |E_p| |F_v|: 2^-7 (1 + 2^-8)
-        // |E_p| |F_v| with room to spare at 1.125 * 2^-7
+        // operands to bf16, plus about 2^-18 of it from the fp32
+        // accumulation (at most R <= 64 roundings of 2^-24), and
+        // sum_k |E_k F_k| <= |E_p| |F_v|: under 1.003 * 2^-7 |E_p| |F_v|,
+        // with room to spare at 1.125 * 2^-7
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * kq + i;
