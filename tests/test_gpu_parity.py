@@ -240,6 +240,15 @@ def test_tight_bound_many_candidates(device, oracle_lib):
         _parity(p, device, oracle_lib, label=f"many candidates mode={mode} W={W} k={k}")
 
 
+def test_fp32_logits_full_vocabulary(device, oracle_lib):
+    """fp32 logits at the Qwen3 vocabulary (the sweep's four-element vectors
+    and a ragged row length), trigram table and coherence planting, in the
+    launch plan of a small batch and of a forced chunk count."""
+    for V, chunks in [(151936, 0), (151937, 3)]:
+        p = synth.make_problem("c3p", 1, B=3, V=V, dtype=synth.DTYPE_F32, hash_cap_log2=16, hash_keys_log2=15)
+        _parity(p, device, oracle_lib, sweep_chunks=chunks, label=f"fp32 V={V} chunks={chunks}")
+
+
 def test_empty_csr_table(device, oracle_lib):
     """A CSR table with no successors at all (nnz = 0, no successor arrays):
     nothing is admitted."""
