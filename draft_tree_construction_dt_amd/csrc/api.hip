@@ -2,6 +2,7 @@
 // host-side validation, launch planning and the two kernel launches.
 // Nothing here allocates, synchronises or keeps state between calls.
 #include <math.h>
+#include <string.h>
 
 #include "common.h"
 
@@ -186,7 +187,11 @@ static dt_status check_ngram(const dt_ngram_table* g) {
 using namespace dt;
 
 extern "C" const char* dt_status_string(dt_status s) {
-    switch (s) {
+    // any int may arrive from C: read the bits without loading an
+    // out-of-range enumeration value
+    int v;
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
     case DT_OK: return "DT_OK";
     case DT_ERR_INVALID_ARG: return "DT_ERR_INVALID_ARG: null pointer, value out of range or misaligned buffer";
     case DT_ERR_UNSUPPORTED: return "DT_ERR_UNSUPPORTED: outside the library's limits";

@@ -29,3 +29,14 @@ def device():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     return torch.device("cuda:0")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """How many compared requests differed from the oracle and were accepted
+    by the step-wise near-tie validator (gpu_util.assert_parity)."""
+    import gpu_util
+    t = gpu_util.NEAR_TIE_TOTAL
+    if t["requests"]:
+        terminalreporter.write_line(
+            f"[near-tie] {t['accepted']} of {t['requests']} compared requests differed from the oracle "
+            f"within the {gpu_util.SCORE_TOL:g} band (every other request matched exactly)")

@@ -214,48 +214,204 @@ def all_valid_paths(p, b: int):
     return out
 
 
-def sketch_build(p, b: int, W: int):
-    """The DARTree page's implementation sketch restated with paths as tuples:
-    every frontier path proposes its position's top-W tokens, all candidates
-    are scored in one batch by their cumulative score, and the best ``width``
-    are kept across the whole frontier.  The sketch's unstable argsort is
-    replaced by a stable order (score desc, token asc, parent position asc).
-    Returns {depth: [paths]} as the sketch does (no N-gram, no budget)."""
-    X = logits_f64(p)
-    ctx1 = int(p.ctx[b, 1])
-    nodes = {0: [()]}
-    score = {(): 0.0}
+def tree_paths(tree: dict, b: int) -> list:
+    """Token path (tuple) of every node of request b, in node order."""
+    n = int(tree["n_nodes"][b])
+    tok, par = tree["tokens"][b], tree["parents"][b]
+    out = []
+    for i in range(n):
+        out.append((out[int(par[i])] if par[i] >= 0 else ()) + (int(tok[i]),))
+    return out
+
+
+class PathScorer:
+    """fp64 keys of token paths of request b, summed from the logits in path
+    order, parent term first: Rk = (Rk_parent + x) + g (the lse-free key the
+    per-depth selection ranks) and S = (S_parent + (x - lse)) + g (the
+    cumulative log-score the verification budget ranks).  g = E[parent token]
+    . F[child] outside DART mode (the DARTree page's P_AR equation, low-rank
+    stand-in)."""
+
+    def __init__(self, p, b: int):
+        self.p, self.b = p, b
+        self.X = logits_f64(p)[b]
+        self.L = [lse_np(self.X[i]) for i in range(p.d)]
+        self.ctx = (int(p.ctx[b, 0]), int(p.ctx[b, 1]))
+        self.memo = {(): (0.0, 0.0)}
+        if p.mode != MODE_DART:
+            self.E = p.E.astype(np.float64)
+            self.F = p.F.astype(np.float64)
+
+    def parent_tokens(self, path):
+        """(grandparent token, parent token) of a child appended to ``path``."""
+        if not path:
+            return self.ctx
+        if len(path) == 1:
+            return self.ctx[1], path[0]
+        return path[-2], path[-1]
+
+    def g(self, ptok: int, c: int) -> float:
+        if self.p.mode == MODE_DART:
+            return 0.0
+        return float(np.dot(self.E[ptok], self.F[c]))
+
+    def keys(self, path):
+        """(Rk, S) of a path."""
+        got = self.memo.get(path)
+        if got is None:
+            rk_p, s_p = self.keys(path[:-1])
+            t, c = len(path), path[-1]
+            x = self.X[t - 1, c]
+            g = self.g(self.parent_tokens(path[:-1])[1], c)
+            got = ((rk_p + x) + g, (s_p + (x - self.L[t - 1])) + g)
+            self.memo[path] = got
+        return got
+
+
+def depth_candidates(p, sc: PathScorer, cont, frontier: list, t: int) -> list:
+    """Every admissible child of the depth t-1 frontier (a list of paths in
+    rank order), per parent rank r: (child tokens ascending, their Rk).
+    Children come from position t-1's top-k (DART Fig. 3), or from the whole
+    vocabulary in DARTREE_FULL mode, with a finite logit and N-gram
+    continuity after the parent's context."""
+    X = sc.X[t - 1]
     full = p.mode == MODE_DARTREE_FULL
+    finite = np.nonzero(np.isfinite(X))[0]
+    pool = finite if full else np.sort(np.array([c for c in topk_np(X, p.k) if np.isfinite(X[c])], dtype=np.int64))
+    out = []
+    for path in frontier:
+        a2, a1 = sc.parent_tokens(path)
+        if cont.kind != NGRAM_NONE:
+            toks = np.array([c for c in pool.tolist() if cont(a2, a1, c)], dtype=np.int64)
+        else:
+            toks = pool
+        rk_p = sc.keys(path)[0]
+        if p.mode == MODE_DART:
+            g = np.zeros(len(toks))
+        elif 0 <= a1 < p.V:
+            g = sc.F[toks] @ sc.E[a1]
+        else:
+            g = np.zeros(len(toks))
+        out.append((toks, (rk_p + X[toks]) + g))
+    return out
+
+
+def check_depth_selection(p, tree: dict, b: int, *, W=None, tol: float = 1e-4, exact: bool = False) -> list:
+    """Step-wise check of the per-depth selection of an unpruned candidate
+    tree (DARTree page, "Tree Construction": after each depth the top-W
+    scored nodes across the entire frontier are kept).  Taking the tree's
+    own depth t-1 as the frontier, depth t must hold min(W, #admissible)
+    admissible children, none of them below an unselected one by more than
+    tol, in key order up to inversions smaller than tol.  Exact keys give a
+    unique answer (ties: token, then parent rank); the band admits the
+    choices an fp64 rounding difference below tol could flip.  With
+    ``exact`` the depth must instead equal the first min(W, #admissible)
+    children in the total order (Rk desc, token asc, parent rank asc).
+    Returns the violated properties (empty when the tree passes)."""
+    W = p.W if W is None else W
+    sc = PathScorer(p, b)
+    cont = Continuity(p.ngram, p.V)
+    paths = tree_paths(tree, b)
+    by_depth = {}
+    for q in paths:
+        by_depth.setdefault(len(q), []).append(q)
+    errs = []
+    frontier = [()]
+    seen = 0
     for t in range(1, p.d + 1):
-        shared = None if full else topk_np(X[b, t - 1], p.k).tolist()
-        cands = []
-        for r, path in enumerate(nodes[t - 1]):
-            ptok = path[-1] if path else ctx1
-            if full:
-                # batch_propose(path, num_drafts=W): this path's own W best
-                # tokens under x + E[ptok] . F[v] over the whole vocabulary
-                g_all = p.F.astype(np.float64) @ p.E[ptok].astype(np.float64)
-                cond = X[b, t - 1] + g_all
-                order = np.lexsort((np.arange(p.V), -cond))
-                props = [int(v) for v in order if X[b, t - 1, v] != -math.inf][:W]
-            else:
-                props = shared
-            for tok in props:
-                x = X[b, t - 1, tok]
-                if x == -math.inf:
-                    continue
-                g = 0.0
-                if p.mode != MODE_DART:
-                    g = float(np.dot(p.E[ptok].astype(np.float64), p.F[tok].astype(np.float64)))
-                cands.append(((score[path] + x) + g, tok, r, path + (tok,)))
-        cands.sort(key=lambda c: (-c[0], c[1], c[2]))
-        nodes[t] = []
-        for rk, tok, r, pth in cands[:W]:
-            score[pth] = rk
-            nodes[t].append(pth)
-        if not nodes[t]:
+        cand = depth_candidates(p, sc, cont, frontier, t)
+        n_cand = sum(len(toks) for toks, _ in cand)
+        sel = by_depth.get(t, [])
+        want = min(W, n_cand)
+        if len(sel) != want:
+            errs.append(f"b{b} depth {t}: {len(sel)} nodes, expected {want}")
+            return errs
+        if not sel:
             break
-    return nodes
+        seen += len(sel)
+        rank = {q: r for r, q in enumerate(frontier)}
+        ks = []
+        taken = [np.zeros(len(toks), dtype=bool) for toks, _ in cand]
+        for q in sel:
+            r = rank.get(q[:-1])
+            toks, rk = cand[r] if r is not None else (np.zeros(0, dtype=np.int64), None)
+            j = int(np.searchsorted(toks, q[-1]))
+            if r is None or j >= len(toks) or toks[j] != q[-1]:
+                errs.append(f"b{b} depth {t}: {q} is not an admissible child of the frontier")
+                return errs
+            taken[r][j] = True
+            ks.append(float(rk[j]))
+        if exact:
+            order = sorted(((-float(v), int(c), r) for r, (toks, rk) in enumerate(cand) for c, v in zip(toks, rk)))
+            best = [frontier[r] + (c,) for _, c, r in order[:want]]
+            if best != sel:
+                errs.append(f"b{b} depth {t}: {sel} is not the exact top-{W} {best}")
+                return errs
+        rest = max((float(np.max(rk[~tk])) for (_, rk), tk in zip(cand, taken) if np.any(~tk)), default=None)
+        if rest is not None and min(ks) < rest - tol:
+            errs.append(f"b{b} depth {t}: selected key {min(ks)} below unselected {rest}")
+        for i in range(len(ks) - 1):
+            if ks[i] < ks[i + 1] - tol:
+                errs.append(f"b{b} depth {t}: nodes {i},{i + 1} out of key order")
+                break
+        frontier = sel
+    if seen != len(paths):
+        errs.append(f"b{b}: {len(paths) - seen} node(s) below the last selected depth")
+    return errs
+
+
+def check_budget_selection(p, tree: dict, cand_tree: dict, b: int, *, budget=None, tol: float = 1e-4,
+                           ref_tree=None) -> list:
+    """Step-wise check of the verification budget (DARTree abstract: best-
+    first pruning selects the verification tree from the fixed-width
+    candidate tree).  ``cand_tree`` is the unpruned candidate tree.  Best-
+    first is replayed over it: at every step the tree's next node must be
+    available (its parent already taken, or depth 1) and its cumulative score
+    S within tol of the best available one; the node taken is the tree's best
+    available node.  With ``ref_tree`` (the exact selection) given in DART
+    mode, where S never rises along a path and the selection is the global
+    top-budget by S, every node in which the two sets differ must also lie
+    within tol of the cut (the budget-th best S).  Returns the violated
+    properties."""
+    budget = p.budget if budget is None else budget
+    sc = PathScorer(p, b)
+    cand = tree_paths(cand_tree, b)
+    kids = {}
+    for q in cand:
+        kids.setdefault(q[:-1], []).append(q)
+    got = tree_paths(tree, b)
+    G = set(got)
+    errs = []
+    if len(cand) <= budget:
+        if G != set(cand):
+            errs.append(f"b{b}: budget does not bind but the node set differs from the candidate tree")
+        return errs
+    if len(got) != budget or len(G) != budget:
+        return [f"b{b}: {len(got)} nodes, expected {budget}"]
+    outside = [q for q in got if q not in set(cand)]
+    if outside:
+        return [f"b{b}: {outside[0]} is not in the candidate tree"]
+    S = {q: sc.keys(q)[1] for q in cand}
+    avail = set(kids.get((), []))
+    for step in range(budget):
+        best = max(S[a] for a in avail)
+        mine = [a for a in avail if a in G]
+        if not mine:
+            errs.append(f"b{b} step {step}: no selected node is available")
+            break
+        pick = max(mine, key=lambda a: S[a])
+        if S[pick] < best - tol:
+            errs.append(f"b{b} step {step}: took S={S[pick]} with {best} available")
+            break
+        avail.discard(pick)
+        avail.update(kids.get(pick, []))
+    if ref_tree is not None and p.mode == MODE_DART:
+        O = set(tree_paths(ref_tree, b))
+        cut = min(S[q] for q in O)
+        off = [q for q in G ^ O if abs(S[q] - cut) > tol]
+        if off:
+            errs.append(f"b{b}: {off[0]} differs from the exact selection {S[off[0]] - cut:+.3g} from the cut")
+    return errs
 
 
 def has_near_ties(values, tol: float) -> bool:

@@ -4,8 +4,9 @@ parent-conditioned distribution x + E[parent] . F[v] (DARTree page, "Tree
 Construction": W candidate tokens per node, all candidates scored in one
 batch, top-W across the frontier), then the usual frontier and budget.
 
-Each pin checks the oracle against something other than itself: the page's
-sketch with per-path proposals, brute force over all one-step extensions,
+Each pin checks the oracle against something other than itself: per-node
+proposals restated from the rule (each node's W best tokens, then the top-W
+of their union), brute force over all one-step extensions,
 the reduction to DART mode when E = F = 0, the greedy decode at W = 1, the
 full V-ary trie, best-first selection restated over the full candidate tree,
 and the invariants of any correct tree.
@@ -18,7 +19,8 @@ import pytest
 
 from draft_tree_construction_dt_amd import synth
 from refcheck import (MODE_DART, MODE_DARTREE_FULL, NGRAM_DENSE_BIGRAM, NGRAM_NONE, all_valid_paths,
-                      check_invariants, has_near_ties, logits_f64, lse_np, paths_of, sketch_build)
+                      check_depth_selection, check_invariants, has_near_ties, logits_f64, lse_np, paths_of,
+                      tree_paths)
 
 
 def _rand(seed, **kw):
@@ -33,19 +35,39 @@ def _g(p, a, c):
 
 
 @pytest.mark.parametrize("seed", range(10))
-def test_matches_sketch_with_per_path_proposals(oracle_lib, seed):
-    """The page's sketch with batch_propose(path, W) = that path's own W best
-    tokens over the vocabulary."""
+def test_union_of_per_node_proposals(oracle_lib, seed):
+    """Reading of the "Tree Construction" rule: every frontier node proposes
+    its own W best tokens of the vocabulary under x + E[its token] . F (key
+    order Rk desc, token asc), and the next frontier is the top-W of the union
+    of all proposals (Rk desc, token asc, parent rank asc).  Restated here
+    with numpy over whole vocabulary rows, per depth, from the oracle's own
+    previous depth; the oracle ranks all (node, token) pairs at once."""
     W = 4
     p = _rand(seed, V=24, d=5, W=W, budget=5 * W, integer_logits=(seed % 2 == 0))
     out = oracle_lib.build_tree(p)
-    nodes = sketch_build(p, 0, W)
-    got = paths_of(out, 0)
-    by_depth = {}
-    for q in sorted(got, key=lambda q: got[q]):
-        by_depth.setdefault(len(q), []).append(q)
+    X = logits_f64(p)[0]
+    E, F = p.E.astype(np.float64), p.F.astype(np.float64)
+    paths = tree_paths(out, 0)
+    rk = {(): 0.0}
+    frontier = [()]
     for t in range(1, p.d + 1):
-        assert by_depth.get(t, []) == nodes.get(t, []), f"depth {t}"
+        props = []
+        for r, path in enumerate(frontier):
+            ptok = path[-1] if path else int(p.ctx[0, 1])
+            key = (rk[path] + X[t - 1]) + F @ E[ptok]
+            live = np.nonzero(np.isfinite(X[t - 1]))[0]
+            mine = live[np.lexsort((live, -key[live]))][:W]
+            props += [(-float(key[c]), int(c), r) for c in mine]
+        props.sort()
+        want = [frontier[r] + (c,) for _, c, r in props[:W]]
+        have = [q for q in paths if len(q) == t]
+        assert have == want, f"depth {t}"
+        for (nk, c, r) in props[:W]:
+            rk[frontier[r] + (c,)] = -nk
+        frontier = have
+        if not have:
+            break
+    assert not check_depth_selection(p, out, 0, tol=0.0, exact=True)
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -53,12 +75,15 @@ def test_bruteforce_top_w_of_all_extensions(oracle_lib, seed):
     """Depth t is the top-W of ALL one-step extensions (every token of the
     vocabulary) of depth t-1: taking each parent's W best first loses
     nothing, since no parent contributes more than W to the top-W."""
-    p = _rand(seed, V=7, d=4, neg_inf_frac=0.1 * (seed % 3))
+    for attempt in range(1000):             # the first draw whose keys are all distinct
+        p = _rand([seed, attempt], V=7, d=4, neg_inf_frac=0.1 * (seed % 3))
+        paths = all_valid_paths(p, 0)
+        if not has_near_ties([v[1] for v in paths.values()], 1e-9):
+            break
+    else:
+        raise AssertionError("no instance without near ties")
     W = 3
     out = oracle_lib.build_tree(p, W=W, budget=p.d * W)
-    paths = all_valid_paths(p, 0)
-    if has_near_ties([v[1] for v in paths.values()], 1e-9):
-        pytest.skip("near tie")
     got = paths_of(out, 0)
     prev = {()}
     for t in range(1, p.d + 1):

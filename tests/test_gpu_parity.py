@@ -141,7 +141,8 @@ def test_random_problems(device, oracle_lib, kind, mode):
         p = synth.random_problem(
             rng, B=int(rng.integers(1, 5)), V=V, d=d, k=k, W=W, budget=budget, ngram=kind, mode=mode,
             dtype=synth.DTYPE_BF16 if trial % 2 else synth.DTYPE_F32, density=0.6,
-            min_logp=-1.5 if kind == NGRAM_DENSE_BIGRAM else (-1.0 if trial % 3 == 0 else -math.inf),
+            # dense rows are log-softmaxes over V: a threshold near -log V admits about half
+            min_logp=(-math.log(V) - 0.5) if kind == NGRAM_DENSE_BIGRAM else (-1.0 if trial % 3 == 0 else -math.inf),
             hash_cap=256, hash_S=int(rng.integers(1, 9)), csr_deg=int(rng.integers(1, 12)),
             neg_inf_frac=0.05 if trial % 4 == 0 else 0.0, integer_logits=trial % 5 == 0, R=8)
         _parity(p, device, oracle_lib, sweep_chunks=int(rng.integers(0, 4)),

@@ -15,7 +15,7 @@ from draft_tree_construction_dt_amd import synth
 from refcheck import (MODE_DART, MODE_DARTREE, NGRAM_CSR_BIGRAM, NGRAM_DENSE_BIGRAM,
                       NGRAM_HASH_TRIGRAM, NGRAM_NONE, Continuity, all_valid_paths,
                       check_invariants, has_near_ties, lse_np, mask_closure, paths_of,
-                      product_count, sketch_build, topk_np, logits_f64)
+                      product_count, topk_np, logits_f64, check_depth_selection)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
 
@@ -123,12 +123,25 @@ def test_topk_with_neg_inf(oracle_lib):
 # P3: brute force over every path of tiny problems
 # --------------------------------------------------------------------------
 
-def _tiny(seed, *, ngram, mode=MODE_DART, V=6, d=3, k=3, integer=False, neg_inf=0.0):
-    rng = np.random.default_rng(seed)
+def _tiny(seed, *, ngram, mode=MODE_DART, V=6, d=3, k=3, integer=False, neg_inf=0.0, attempt=0):
+    rng = np.random.default_rng([seed, attempt])
     return synth.random_problem(rng, B=1, V=V, d=d, k=k, W=1, budget=1, ngram=ngram,
                                 min_logp=-1.5 if ngram == NGRAM_DENSE_BIGRAM else -math.inf,
                                 mode=mode, density=0.6, integer_logits=integer,
                                 neg_inf_frac=neg_inf, hash_cap=64, hash_S=3, csr_deg=4)
+
+
+def _tiny_nondegenerate(seed, *, ngram, mode=MODE_DART, key=0, min_paths=3):
+    """The first draw of the seed's sequence with at least ``min_paths``
+    admissible paths and no two of them closer than 1e-9 in key ``key``
+    (0: the score S, 1: the rank key Rk), so that the expected answer is
+    unique.  Draws with a trigram table admit few paths, hence the retries."""
+    for attempt in range(1000):
+        p = _tiny(seed, ngram=ngram, mode=mode, attempt=attempt)
+        paths = all_valid_paths(p, 0)
+        if len(paths) >= min_paths and not has_near_ties([v[key] for v in paths.values()], 1e-9):
+            return p, paths
+    raise AssertionError("no non-degenerate instance in 1000 draws")
 
 
 KINDS = [NGRAM_NONE, NGRAM_DENSE_BIGRAM, NGRAM_CSR_BIGRAM, NGRAM_HASH_TRIGRAM]
@@ -155,10 +168,7 @@ def test_bruteforce_full_trie(oracle_lib, kind, seed):
 def test_bruteforce_budget_is_top_prefix_closed(oracle_lib, kind, seed):
     """W unbounded, budget binding (DART mode): best-first keeps the top-budget
     admissible paths by cumulative score, and that set is prefix closed."""
-    p = _tiny(seed, ngram=kind)
-    paths = all_valid_paths(p, 0)
-    if len(paths) < 3 or has_near_ties([v[0] for v in paths.values()], 1e-9):
-        pytest.skip("degenerate instance")
+    p, paths = _tiny_nondegenerate(seed, ngram=kind, key=0, min_paths=4)
     budget = len(paths) // 2
     out = oracle_lib.build_tree(p, W=p.k ** p.d, budget=budget)
     want = sorted(paths, key=lambda q: -paths[q][0])[:budget]
@@ -174,12 +184,9 @@ def test_bruteforce_width_per_depth(oracle_lib, kind, mode, seed):
     """W binding, budget unbounded: depth t holds the top-W admissible one-step
     extensions of depth t-1 (all V tokens enumerated, top-k membership
     checked per edge)."""
-    p = _tiny(seed, ngram=kind, mode=mode)
+    p, paths = _tiny_nondegenerate(seed, ngram=kind, mode=mode, key=1)
     W = 2
     out = oracle_lib.build_tree(p, W=W, budget=p.d * W)
-    paths = all_valid_paths(p, 0)
-    if has_near_ties([v[1] for v in paths.values()], 1e-9):
-        pytest.skip("near tie")
     got = paths_of(out, 0)
     prev = {()}
     for t in range(1, p.d + 1):
@@ -270,24 +277,29 @@ def test_mask_is_warshall_closure(oracle_lib, seed):
 
 
 # --------------------------------------------------------------------------
-# P6: the DARTree page's sketch, restated with tuples
+# P6: every depth is the exact top-W of its frontier's admissible children
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("mode", [MODE_DART, MODE_DARTREE])
-@pytest.mark.parametrize("seed", range(10))
-def test_matches_dartree_sketch(oracle_lib, mode, seed):
-    rng = np.random.default_rng(seed)
-    W = 4
-    p = synth.random_problem(rng, B=1, V=20, d=5, k=W, W=W, budget=5 * W, mode=mode, R=4,
-                             integer_logits=(seed % 2 == 0))
+@pytest.mark.parametrize("seed", range(6))
+def test_depths_are_exact_top_w_of_their_frontier(oracle_lib, kind, mode, seed):
+    """The DARTree page's "Tree Construction" rule restated as a check: with
+    the budget not binding, depth t of the oracle's tree is the first
+    min(W, #admissible) children of depth t-1 in the order (Rk desc, token
+    asc, parent rank asc), keys summed in fp64 from the logits (and the
+    parent term) by the checker itself.  Problems larger than the brute-force
+    pins can enumerate, integer logits for exact ties in half of them."""
+    rng = np.random.default_rng(1000 + 10 * kind + mode * 100 + seed)
+    W = int(rng.integers(2, 9))
+    d = int(rng.integers(2, 6))
+    p = synth.random_problem(rng, B=2, V=int(rng.integers(20, 80)), d=d, k=int(rng.integers(2, 9)), W=W,
+                             budget=d * W, ngram=kind, mode=mode, R=4, density=0.7,
+                             min_logp=-1.5 if kind == NGRAM_DENSE_BIGRAM else -math.inf,
+                             hash_cap=1024, hash_S=6, csr_deg=10, integer_logits=(seed % 2 == 0))
     out = oracle_lib.build_tree(p)
-    nodes = sketch_build(p, 0, W)
-    got = paths_of(out, 0)
-    by_depth = {}
-    for q in sorted(got, key=lambda q: got[q]):
-        by_depth.setdefault(len(q), []).append(q)
-    for t in range(1, p.d + 1):
-        assert by_depth.get(t, []) == nodes.get(t, []), f"depth {t}"
+    for b in range(p.B):
+        assert not check_depth_selection(p, out, b, tol=0.0, exact=True)
 
 
 # --------------------------------------------------------------------------
