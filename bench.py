@@ -57,8 +57,13 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--streams", type=int, default=4,
                     help="HIP streams the calls alternate over (consecutive batches in flight together)")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="bracket every n-th B=64 sweep launch with timing events")
+    ap.add_argument("--event-every", type=int, default=1,
+                    help="bracket every n-th B=64 sweep launch of the one-stream pass with timing events")
+    ap.add_argument("--one-stream-calls", type=int, default=200,
+                    help="least number of calls in the one-stream pass (its sweep launches are the roofline "
+                         "samples), whatever --steps is")
+    ap.add_argument("--cpu-procs", type=int, default=0,
+                    help="worker processes of the multi-process oracle run (0 = the host's cores, at most 16)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--update-steps", type=int, default=2000, help="timed trigram-table update calls")
     ap.add_argument("--sweep-chunks", type=int, default=0, help="0 = the library's automatic plan")
@@ -209,6 +214,80 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_slice(args):
+    """Worker of the multi-process oracle run: build the trees of requests
+    [lo, hi) of the shared problem (inherited from the parent by fork)."""
+    lo, hi = args
+    import oracle
+    p = _CPU_PROB
+    sub = copy.copy(p)
+    sub.B = hi - lo
+    sub.logits = p.logits[lo:hi]
+    sub.ctx = p.ctx[lo:hi]
+    oracle.build_tree(sub)
+    return hi - lo
+
+
+_CPU_PROB = None
+
+
+def cpu_baseline(prob, sample: int, procs: int) -> dict:
+    """The oracle as it stands, on this host's cores: the first ``sample``
+    requests on one thread, and every request of the input sets spread over
+    worker processes (one slice of requests each; the oracle is
+    single-threaded C).  Runs before the GPU is initialised."""
+    import multiprocessing as mp
+    import oracle
+    global _CPU_PROB
+    n = max(1, min(sample, prob.B))
+    sub = copy.copy(prob)
+    sub.B = n
+    sub.logits = prob.logits[:n]
+    sub.ctx = prob.ctx[:n]
+    tc = time.perf_counter()
+    oracle.build_tree(sub)
+    one_s = time.perf_counter() - tc
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    nproc = max(1, min(procs or cores, 16, prob.B))
+    _CPU_PROB = prob
+    per = -(-prob.B // nproc)
+    slices = [(lo, min(prob.B, lo + per)) for lo in range(0, prob.B, per)]
+    ctx = mp.get_context("fork")
+    tm = time.perf_counter()
+    with ctx.Pool(nproc) as pool:
+        done = sum(pool.map(_oracle_slice, slices))
+    multi_s = time.perf_counter() - tm
+    _CPU_PROB = None
+    print(f"[bench] oracle: {n} trees on 1 thread in {one_s:.1f}s, {done} trees on {nproc} processes in "
+          f"{multi_s:.1f}s", file=sys.stderr, flush=True)
+    return {
+        "value": n / one_s,
+        "unit": "trees/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"the first {n} requests of the input sets (whole path: normaliser, top-k, trigram expansion, "
+                  f"top-W, budget, mask), single-threaded C, {one_s:.1f}s",
+        "cpu_model": cpu_model(),
+        "host_cores": cores,
+        "multi": {
+            "value": done / multi_s, "unit": "trees/s", "cores": nproc, "kind": "oracle",
+            "sample": f"all {done} requests of the input sets over {nproc} worker processes (one slice of "
+                      f"requests each, process start-up included), {multi_s:.1f}s",
+        },
+    }
+
+
 def run_workload(args) -> None:
     """Per-call latency of one named configuration: calls on one stream, each
     bracketed by fence-free events, inputs rotated over enough distinct sets
@@ -329,7 +408,8 @@ def run_workload(args) -> None:
         oracle.build_tree(sample)
         cpu_s = time.perf_counter() - tc
         res["cpu_baseline"] = {"value": n / cpu_s, "unit": "trees/s", "cores": 1, "kind": "oracle",
-                               "sample": f"the first {n} requests, single-threaded C, {cpu_s:.2f}s"}
+                               "sample": f"the first {n} requests, single-threaded C, {cpu_s:.2f}s",
+                               "cpu_model": cpu_model()}
     print(json.dumps(res), flush=True)
 
 
@@ -412,14 +492,19 @@ def main():
         run_workload(args)
         return
 
-    import torch
-    from draft_tree_construction_dt_amd import binding as bd
-
-    dev = torch.device("cuda:0")
     t0 = time.time()
     prob = make_workload(args.sets, args.seed)
     gen_s = time.time() - t0
     print(f"[bench] generated {args.sets} input sets in {gen_s:.1f}s", file=sys.stderr, flush=True)
+    # the oracle's timing runs first, before anything touches the GPU (its
+    # worker processes are forked from this one)
+    cpu = None if args.no_cpu else cpu_baseline(prob, args.cpu_sample, args.cpu_procs)
+
+    import statistics
+    import torch
+    from draft_tree_construction_dt_amd import binding as bd
+
+    dev = torch.device("cuda:0")
 
     logits = bd.logits_tensor(prob, dev)                      # [sets*64][d][V] bf16
     ctx = torch.from_numpy(prob.ctx).to(dev)
@@ -493,9 +578,13 @@ def main():
     t_total, _ = run(BATCH, set_first, K, args.warmup, nstream)
     ms_per_step = t_total / K * 1e3
     trees_per_s = BATCH * K / t_total
-    # one stream: the kernels run alone, so the sweep events time the kernel itself
-    t_one, sweep_ms = run(BATCH, set_first, K, args.warmup, 1, events_every=every)
+    # one stream: the kernels run alone, so the sweep events time the kernel
+    # itself; at least --one-stream-calls calls, so the roofline figure does
+    # not hang on a handful of launches
+    K_one = max(K, args.one_stream_calls)
+    t_one, sweep_ms = run(BATCH, set_first, K_one, args.warmup, 1, events_every=every)
     sweep_avg_s = sum(sweep_ms) / len(sweep_ms) / 1e3
+    sweep_sorted = sorted(sweep_ms)
 
     # ---- B = 1: one request per call, rotating over every request of every set
     nreq = BATCH * args.sets
@@ -583,9 +672,11 @@ def main():
         "us_per_tree": t_total / (BATCH * K) * 1e6,
         "streams": nstream,
         "single_stream": {
-            "trees_per_s": BATCH * K / t_one,
-            "ms_per_step": t_one / K * 1e3,
-            "us_per_tree": t_one / (BATCH * K) * 1e6,
+            "trees_per_s": BATCH * K_one / t_one,
+            "ms_per_step": t_one / K_one * 1e3,
+            "us_per_tree": t_one / (BATCH * K_one) * 1e6,
+            "steps": K_one,
+            "hbm_frac_whole_call": logit_bytes / (t_one / K_one) / 1e9 / HBM_PEAK_GBS,
         },
         "b1": {
             "workload": "same shape, B=1 (one request per call)",
@@ -616,31 +707,19 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
             "avg_launch_us": sweep_avg_s * 1e6,
+            "median_launch_us": statistics.median(sweep_ms) * 1e3,
+            "p10_launch_us": sweep_sorted[len(sweep_sorted) // 10] * 1e3,
+            "p90_launch_us": sweep_sorted[(9 * len(sweep_sorted)) // 10] * 1e3,
+            "samples": len(sweep_ms),
             "timing": f"HIP events recorded by the library around every {every}-th sweep launch of the "
                       f"one-stream timed loop ({len(sweep_ms)} launches) on its stream, created with "
-                      f"hipEventDisableSystemFence",
+                      f"hipEventDisableSystemFence; achieved = algorithmic bytes / the mean duration",
             "algorithmic_bytes_per_launch": logit_bytes,
         },
     }
 
-    if not args.no_cpu:
-        import oracle
-        n = max(1, min(args.cpu_sample, prob.B))
-        sample = copy.copy(prob)
-        sample.B = n
-        sample.logits = prob.logits[:n]
-        sample.ctx = prob.ctx[:n]
-        tc = time.perf_counter()
-        oracle.build_tree(sample)
-        cpu_s = time.perf_counter() - tc
-        res["cpu_baseline"] = {
-            "value": n / cpu_s,
-            "unit": "trees/s",
-            "cores": 1,
-            "kind": "oracle",
-            "sample": f"the first {n} requests of the input sets, {-(-n // BATCH)} batch(es) of {BATCH} (whole path: normaliser, top-k, "
-                      f"trigram expansion, top-W, budget, mask), single-threaded C, {cpu_s:.1f}s",
-        }
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
