@@ -67,8 +67,9 @@ class _TreeOut(ctypes.Structure):
                 ("scores", ctypes.c_void_p), ("mask", ctypes.c_void_p)]
 
 
-EXPORTED = ("dt_build_tree", "dt_workspace_size", "dt_status_string", "dt_position_topk", "dt_ngram_update",
-            "dt_verify_length")
+EXPORTED = ("dt_build_tree", "dt_build_tree_noalloc", "dt_workspace_size", "dt_status_string", "dt_position_topk",
+            "dt_ngram_update", "dt_verify_length")
+DT_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -87,6 +88,8 @@ def _load():
         lib.dt_build_tree.restype = ctypes.c_int
         lib.dt_build_tree.argtypes = [ctypes.c_void_p, ctypes.POINTER(_NGram), ctypes.POINTER(_Params),
                                       ctypes.POINTER(_TreeOut)]
+        lib.dt_build_tree_noalloc.restype = ctypes.c_int
+        lib.dt_build_tree_noalloc.argtypes = lib.dt_build_tree.argtypes
         lib.dt_workspace_size.restype = ctypes.c_size_t
         lib.dt_workspace_size.argtypes = [ctypes.POINTER(_Params)]
         lib.dt_status_string.restype = ctypes.c_char_p
@@ -217,6 +220,15 @@ def dt_build_tree(logits: torch.Tensor, ngram: NGram, params: Params, out: TreeO
     st = _load().dt_build_tree(_ptr(logits), ctypes.byref(g), ctypes.byref(p), ctypes.byref(o))
     if st != DT_OK:
         raise DtError(st, "dt_build_tree")
+
+
+def dt_build_tree_noalloc(logits: torch.Tensor, ngram: NGram, params: Params, out: TreeOut) -> None:
+    """dt_build_tree on the library's own per-GPU scratch array (params.workspace
+    is ignored): for callers that cannot allocate."""
+    g, p, o = ngram._c(), params._c(), out._c()
+    st = _load().dt_build_tree_noalloc(_ptr(logits), ctypes.byref(g), ctypes.byref(p), ctypes.byref(o))
+    if st != DT_OK:
+        raise DtError(st, "dt_build_tree_noalloc")
 
 
 def dt_ngram_update(ngram: "NGram", ctx: torch.Tensor, tokens: torch.Tensor, lengths: torch.Tensor,

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace dt {
@@ -339,8 +341,14 @@ static dt_status build_full(const void* logits, const dt_params* p, const SweepP
     return DT_OK;
 }
 
-extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngram,
-                                   const dt_params* p, const dt_tree_out* out) {
+static dt_status enqueue_build(const void* logits, const dt_ngram_table* ngram, const dt_params* p,
+                               const dt_tree_out* out);
+
+// Every argument check of dt_build_tree except the workspace's; host only.
+// DT_OK with *nothing = true means a valid call with nothing to enqueue (B = 0).
+static dt_status check_build(const void* logits, const dt_ngram_table* ngram, const dt_params* p,
+                             const dt_tree_out* out, bool* nothing) {
+    *nothing = false;
     dt_status st = check_shape(p);
     if (st != DT_OK) return st;
     if ((st = check_ngram(ngram)) != DT_OK) return st;
@@ -358,12 +366,72 @@ extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngr
     }
     const TreePlan plan = plan_tree(p, ngram->kind);
     if (plan.total > kTreeLdsLimit) return DT_ERR_UNSUPPORTED;
-    if (p->B == 0) return DT_OK;
+    if (p->B == 0) {
+        *nothing = true;
+        return DT_OK;
+    }
     if (!logits || ((uintptr_t)logits & 15u) || !p->ctx) return DT_ERR_INVALID_ARG;
     if (!out->n_nodes || !out->tokens || !out->parents || !out->depths || !out->scores || !out->mask)
         return DT_ERR_INVALID_ARG;
-    if ((st = check_workspace(p)) != DT_OK) return st;
+    return DT_OK;
+}
 
+extern "C" dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngram,
+                                   const dt_params* p, const dt_tree_out* out) {
+    bool nothing;
+    dt_status st = check_build(logits, ngram, p, out, &nothing);
+    if (st != DT_OK || nothing) return st;
+    if ((st = check_workspace(p)) != DT_OK) return st;
+    return enqueue_build(logits, ngram, p, out);
+}
+
+// The scratch buffer of dt_build_tree_noalloc: a device array of fixed size
+// in this library's code object, one copy per GPU, held until the process
+// ends.  Host code never passes the array's own name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address of each
+// GPU's copy comes from hipGetSymbolAddress, looked up once per device on
+// the first call there and kept below.
+static __device__ __align__(256) unsigned char scratch[DT_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+static dt_status scratch_of(hipStream_t stream, void** ptr_out) {
+    int dev = 0;
+    if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess) return DT_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return DT_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return DT_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return DT_ERR_HIP;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return DT_ERR_HIP;
+        if (e != hipSuccess || !ptr) return DT_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *ptr_out = g_scratch_ptr[dev];
+    return DT_OK;
+}
+
+extern "C" dt_status dt_build_tree_noalloc(const void* logits, const dt_ngram_table* ngram,
+                                           const dt_params* p, const dt_tree_out* out) {
+    bool nothing;
+    dt_status st = check_build(logits, ngram, p, out, &nothing);
+    if (st != DT_OK || nothing) return st;
+    if (plan_workspace(p, plan_sweep(p)).total > (size_t)DT_NOALLOC_SCRATCH_BYTES) return DT_ERR_WORKSPACE;
+    dt_params q = *p;
+    if ((st = scratch_of((hipStream_t)p->stream, &q.workspace)) != DT_OK) return st;
+    q.workspace_bytes = DT_NOALLOC_SCRATCH_BYTES;
+    return enqueue_build(logits, ngram, &q, out);
+}
+
+// Launches of the whole path for validated arguments and a large enough workspace.
+static dt_status enqueue_build(const void* logits, const dt_ngram_table* ngram, const dt_params* p,
+                               const dt_tree_out* out) {
+    dt_status st;
+    const TreePlan plan = plan_tree(p, ngram->kind);
     const SweepPlan s = plan_sweep(p);
     const WorkspacePlan w = plan_workspace(p, s);
     if (p->mode == DT_MODE_DARTREE_FULL) {

@@ -71,7 +71,8 @@
  *     structs themselves are host memory read during the call only.
  *   - The caller owns every buffer, including the workspace.  The library
  *     never allocates, frees or synchronises, and keeps no state between
- *     calls.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     calls (dt_build_tree_noalloc aside: it holds its scratch array per
+ *     GPU).  Work is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and the call returns without waiting.  Calls on different
  *     streams need different workspaces.
  *   - Arguments are validated on the host before anything is enqueued; on
@@ -185,6 +186,25 @@ typedef struct dt_tree_out {
  * logits: device [B][d][V] of dtype, rows contiguous, 16-byte aligned. */
 dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngram,
                         const dt_params* params, const dt_tree_out* out);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation as dt_build_tree, same arguments except that params->workspace
+ * and params->workspace_bytes are ignored.  The workspace is instead a
+ * scratch array of DT_NOALLOC_SCRATCH_BYTES bytes inside the library, one
+ * copy per GPU (the device of params->stream, or the current device for
+ * the null stream), held from the first call on that GPU until the process
+ * ends.  The call allocates nothing and calls no allocating routine; its
+ * first call on a GPU looks the array's address up (hipGetSymbolAddress).
+ * Every call on one GPU shares that GPU's array: calls whose executions
+ * overlap on the same GPU (different streams, or different host threads)
+ * race and give undefined trees, so serialise them (one stream, or events).
+ * Errors: as dt_build_tree, and DT_ERR_WORKSPACE when dt_workspace_size()
+ * of the parameters exceeds DT_NOALLOC_SCRATCH_BYTES; DT_ERR_HIP when the
+ * device or the array's address cannot be obtained. */
+#define DT_NOALLOC_SCRATCH_BYTES (32u << 20)
+dt_status dt_build_tree_noalloc(const void* logits, const dt_ngram_table* ngram,
+                                const dt_params* params, const dt_tree_out* out);
 
 /* Bytes of workspace dt_build_tree / dt_position_topk need for these
  * parameters (depends on B, V, d, k, mode, dtype and sweep_chunks only, and

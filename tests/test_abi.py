@@ -188,3 +188,25 @@ def test_verify_length_validation():
     assert call(tree=bd._TreeOut(FAKE, FAKE, 0, FAKE, FAKE, FAKE)) == bd.DT_ERR_INVALID_ARG
     assert call(budget=2048) == bd.DT_ERR_UNSUPPORTED
     assert call(B=0) == bd.DT_OK                                            # nothing to do: no launch
+
+
+def _noalloc(params, **kw):
+    p = params._c()
+    p.ctx = FAKE
+    g = bd.NGram()._c()
+    o = bd._TreeOut(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    return bd._load().dt_build_tree_noalloc(kw.get("logits", FAKE), ctypes.byref(g), ctypes.byref(p), ctypes.byref(o))
+
+
+def test_noalloc_validation_before_any_device_call():
+    """dt_build_tree_noalloc validates like dt_build_tree, ignores the
+    caller's workspace fields, and refuses parameters whose workspace would
+    not fit its scratch array, all before touching a device (this machine
+    has none)."""
+    assert _noalloc(_params(B=-1)) == bd.DT_ERR_INVALID_ARG
+    assert _noalloc(_params(k=33)) == bd.DT_ERR_UNSUPPORTED
+    assert _noalloc(_params(), logits=FAKE + 4) == bd.DT_ERR_INVALID_ARG
+    assert _noalloc(_params(B=0)) == bd.DT_OK
+    big = _params(B=1024, V=1000, d=32, k=32, W=32, budget=1024)     # room for 30,753 trigram contexts each
+    assert bd.dt_workspace_size(big) > bd.DT_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(big) == bd.DT_ERR_WORKSPACE
