@@ -438,9 +438,8 @@ static dt_status enqueue_build(const void* logits, const dt_ngram_table* ngram, 
         if (w.C2 > kMaxVocabChunks) return DT_ERR_UNSUPPORTED;   // cannot happen: chunks adapt to V
         return build_full(logits, p, s, w, out);
     }
-    if ((st = launch_sweep_for(logits, p, s, w)) != DT_OK) return st;
-
     char* ws = (char*)p->workspace;
+    if ((st = launch_sweep_for(logits, p, s, w)) != DT_OK) return st;
     PrepArgs pa{};
     pa.B = p->B;
     pa.d = p->d;

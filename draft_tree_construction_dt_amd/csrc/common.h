@@ -287,4 +287,5 @@ hipError_t launch_seed1(const FrontierArgs& a, const int32_t* ctx, hipStream_t s
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 
+
 }  // namespace dt

@@ -1,0 +1,816 @@
+// Device code of the tree step (the prep, tree and merge kernels of
+// tree.hip): the row merge, the N-gram continuity lookups, the depth loop
+// (frontier-wide top-W), the verification budget and the output stage.  The
+// algorithm is described at the top of tree.hip.
+#pragma once
+
+#include "common.h"
+#include "wave.h"
+
+namespace dt {
+namespace treedev {
+typedef double v4d __attribute__((ext_vector_type(4)));
+constexpr unsigned long long kEmptyKey = 0xFFFFFFFFFFFFFFFFull;
+
+__device__ __forceinline__ float key_value(unsigned long long key) {
+    return __uint_as_float(unord_bits((uint32_t)(key >> 32)));
+}
+__device__ __forceinline__ uint32_t key_id(unsigned long long key) { return ~(uint32_t)key; }
+
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+
+__device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
+    // SplitMix64 output function (Steele, Lea, Flood).
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// ---------------------------------------------------------------------------
+// one wave merges the L partial lists of one row
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void merge_row(const float* __restrict__ part_m, const double* __restrict__ part_s,
+                          const unsigned long long* __restrict__ part_keys, int64_t row, int L, int k,
+                          unsigned long long* scratch, int lane, double* lse_out, int* tok_out,
+                          float* val_out) {
+    const float* pm = part_m + row * L;
+    const double* ps = part_s + row * L;
+    const unsigned long long* keys = part_keys + row * (int64_t)L * k;
+    const int n = L * k;
+    // all loads of the row are independent: issue them together
+    float mc[4];
+    double sc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = lane + 64 * q;
+        mc[q] = c < L ? pm[c] : -INFINITY;
+        sc[q] = c < L ? ps[c] : 0.0;
+    }
+    unsigned long long kv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        kv[q] = e < n ? keys[e] : 0ull;
+    }
+
+    // normaliser: max and rescaled sum over the lists, log in fp64
+    const float M = wave_max_f32(fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3])));
+    double sum = 0.0;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (mc[q] != -INFINITY) sum += sc[q] * (double)__builtin_amdgcn_exp2f((mc[q] - M) * 1.4426950408889634f);
+    }
+    sum = wave_add_f64(sum);
+    if (lane == 0) {
+        // the true normaliser is >= the row max; clamp the rounding of a sum
+        // whose largest term is 1 so that every log-probability stays <= 0
+        const double l = log(sum);
+        *lse_out = (M == -INFINITY) ? -INFINITY : (double)M + (l > 0.0 ? l : 0.0);
+    }
+
+    // top-k.  Lower bounds for the row's k-th key, both from k distinct keys:
+    // the k-th key of any full list, and the q-th key of every list holding
+    // q = ceil(k/L) keys when there are enough such lists.
+    const int q = (k + L - 1) / L;
+    unsigned long long bk = 0ull, bq = ~0ull;
+    int nq = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int e = lane + 64 * r;
+        if (e < n) {
+            const int i = e % k;
+            if (i == k - 1) bk = kv[r] > bk ? kv[r] : bk;
+            if (i == q - 1 && kv[r] != 0ull) {
+                bq = kv[r] < bq ? kv[r] : bq;
+                ++nq;
+            }
+        }
+    }
+    bk = wave_max_u64(bk);
+    bq = wave_min_u64(bq);
+    nq = wave_add_i32(nq);
+    unsigned long long th = bk;
+    if (nq * q >= k && bq > th) th = bq;
+    int ns = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool keep = kv[r] != 0ull && kv[r] >= th;
+        const unsigned long long bal = __ballot(keep);
+        if (keep) scratch[ns + lanes_below(bal)] = kv[r];
+        ns += __popcll(bal);
+    }
+    // pad to a multiple of eight with empty keys (0 is below every key)
+    const int ns8 = (ns + 7) & ~7;
+    if (lane < ns8 - ns) scratch[ns + lane] = 0ull;
+    __builtin_amdgcn_wave_barrier();
+    // rank: lane e holds survivor e (blocks of 64) and streams past all of
+    // them, eight independent broadcast reads per step (keys are unique)
+    for (int e0 = 0; e0 < ns; e0 += 64) {
+        const int e = e0 + lane;
+        const unsigned long long v = e < ns ? scratch[e] : ~0ull;
+        int rank = 0;
+        for (int j = 0; j < ns8; j += 8) {
+            unsigned long long o[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o[u] = scratch[j + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rank += o[u] > v;
+        }
+        if (e < ns && rank < k) {
+            tok_out[rank] = (int)key_id(v);
+            val_out[rank] = key_value(v);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// continuity
+// ---------------------------------------------------------------------------
+// Children of one depth by token: an open-addressing table in LDS
+// (kChildSlots slots, load <= 1/4) maps a token to its index in T_{t-1}.
+constexpr int kChildSlots = 128;
+__device__ __forceinline__ uint32_t child_hash(int tok) { return ((uint32_t)tok * 2654435761u) >> 25; }
+
+// Index in T_{t-1} of token s, or -1.
+__device__ __forceinline__ int child_index(const int* ctok, const int* cj, int s) {
+    if (s < 0) return -1;
+    uint32_t pos = child_hash(s);
+    for (int probe = 0; probe < kChildSlots; ++probe) {
+        const int t = ctok[pos];
+        if (t == s) return cj[pos];
+        if (t == -1) return -1;
+        pos = (pos + 1) & (kChildSlots - 1);
+    }
+    return -1;
+}
+
+// OR over the four lanes of a quad (DPP quad permutations, no LDS traffic)
+__device__ __forceinline__ uint32_t quad_or(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    return v;
+}
+
+// Successors 4g .. 4g+3 of a 16-wide chunk of a row (-1 past its end):
+// one 16-byte load when the row allows it.
+__device__ __forceinline__ void load_succ4(int (&r)[4], const int* row, int from, int n) {
+    typedef int i4 __attribute__((ext_vector_type(4)));
+    const int* p = row + from;
+    if (from + 4 <= n && ((uintptr_t)p & 15u) == 0) {
+        const i4 x = *reinterpret_cast<const i4*>(p);
+        r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = from + u < n ? p[u] : -1;
+    }
+}
+
+// Admissible children of the trigram context (a2, a1), computed by the four
+// lanes of a quad together (g = lane & 3): lane g probes slots 2g and 2g+1 of
+// every window of 8 probe positions and holds successors 4g..4g+3 of every 16
+// of the row, and each successor is mapped to its child index through the
+// LDS table.  The first window and the home slot's row are read at once, so a
+// key found in its home slot costs one memory round trip.  Inactive quads
+// (`active` false in all four lanes) read in bounds and return 0.  The
+// result is the same in all four lanes.
+__device__ __forceinline__ uint32_t quad_admitted(const NGramArgs& a, int a2, int a1, bool active, int g,
+                                  const int* ctok, const int* cj, uint32_t live) {
+    const unsigned long long key = ((unsigned long long)(uint32_t)a2 << 32) | (uint32_t)a1;
+    const long long cm = a.cap - 1;
+    const long long home = active ? (long long)(mix64(key) & (unsigned long long)cm) : 0;
+    const int S = a.S;
+    // trip 1: probe window 0 and the first 16 successors of the home slot
+    unsigned long long k0 = a.keys[(home + 2 * g) & cm], k1 = a.keys[(home + 2 * g + 1) & cm];
+    int spec[4];
+    load_succ4(spec, a.succ + home * S, 4 * g, S);
+    long long slot = -1;
+    bool done = !active;
+    for (long long w0 = 0; !done; w0 += 8) {
+        if (w0 > 0) {
+            k0 = a.keys[(home + w0 + 2 * g) & cm];
+            k1 = a.keys[(home + w0 + 2 * g + 1) & cm];
+        }
+        // probe order within the window: slot 2g + e of lane g
+        const uint32_t hitm = (uint32_t)(k0 == key) | ((uint32_t)(k1 == key) << 1);
+        const uint32_t endm = hitm | (uint32_t)(k0 == kEmptyKey) | ((uint32_t)(k1 == kEmptyKey) << 1);
+        const uint32_t F = quad_or(endm << (2 * g)), M = quad_or(hitm << (2 * g));
+        if (F != 0u) {
+            const int idx = __builtin_ctz(F);
+            if ((M >> idx) & 1u) slot = (home + w0 + idx) & cm;
+            done = true;
+        } else if (w0 + 8 >= a.cap) {
+            done = true;                                      // every slot seen: absent
+        }
+    }
+    if (slot < 0) return 0u;
+    const bool membership = a.min_logp == -INFINITY || a.hash_logp == nullptr;
+    const int* row = a.succ + slot * S;
+    uint32_t hit = 0;
+    for (int c0 = 0; c0 < S; c0 += 16) {
+        int sv[4];
+        if (c0 == 0 && slot == home) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sv[u] = spec[u];
+        } else {
+            load_succ4(sv, row, c0 + 4 * g, S);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = child_index(ctok, cj, sv[u]);
+            if (j >= 0 && (membership || a.hash_logp[slot * S + c0 + 4 * g + u] > a.min_logp)) hit |= 1u << j;
+        }
+    }
+    return quad_or(hit) & live;
+}
+
+// Admissible children after the bigram context a1, by the four lanes of a
+// quad (g = lane & 3): a dense row is read at the children's columns (lane g
+// takes children g, g+4, ...); a CSR row is read 64 successors per round
+// trip (lane g takes 4g..4g+3 of every 16), each mapped to its child index
+// through the LDS token table.  Inactive quads and ids outside [0, V) admit
+// nothing.  The result is the same in all four lanes.
+__device__ __forceinline__ uint32_t quad_admitted_bigram(const NGramArgs& a, int a1, bool active, int g, const int* ch,
+                                         const int* ctok, const int* cj, uint32_t live, int k) {
+    if (!active || a1 < 0 || a1 >= a.V) return 0u;               // the same in the whole quad
+    uint32_t hit = 0;
+    if (a.kind == DT_NGRAM_DENSE_BIGRAM) {
+        const float* row = a.dense + (int64_t)a1 * a.V;
+        float v[kMaxK / 4];
+#pragma unroll
+        for (int u = 0; u < kMaxK / 4; ++u) {
+            const int j = g + 4 * u;
+            v[u] = j < k ? row[ch[j]] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < kMaxK / 4; ++u) {
+            const int j = g + 4 * u;
+            if (j < k && v[u] > a.min_logp) hit |= 1u << j;
+        }
+    } else {
+        const int lo = a.row_ptr[a1], hi = a.row_ptr[a1 + 1];
+        const bool membership = a.min_logp == -INFINITY || a.csr_logp == nullptr;
+        for (int e0 = lo; e0 < hi; e0 += 64) {
+            int sv[16];
+            float lp[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int e = e0 + 16 * (u >> 2) + 4 * g + (u & 3);
+                sv[u] = e < hi ? a.col[e] : -1;
+                lp[u] = (!membership && e < hi) ? a.csr_logp[e] : INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int j = child_index(ctok, cj, sv[u]);
+                if (j >= 0 && (membership || lp[u] > a.min_logp)) hit |= 1u << j;
+            }
+        }
+    }
+    return quad_or(hit) & live;
+}
+
+// Index of a continuity context.  Depth t's contexts: bigram -> parent token
+// (t = 1: the root; t >= 2: T_{t-2}[i1]); trigram -> (grandparent, parent)
+// (t = 1: (ctx0, ctx1); t = 2: (ctx1, T_0[i1]); t >= 3: (T_{t-3}[i2], T_{t-2}[i1])).
+__device__ __forceinline__ int ctx_index(int kind, int k, int t, int i2, int i1) {
+    if (t == 1) return 0;
+    if (kind == DT_NGRAM_HASH_TRIGRAM) {
+        if (t == 2) return 1 + i1;
+        return 1 + k + (t - 3) * k * k + i2 * k + i1;
+    }
+    return 1 + (t - 2) * k + i1;
+}
+
+// ---------------------------------------------------------------------------
+// ordering keys
+// ---------------------------------------------------------------------------
+// budget: (S desc, depth asc, BFS index asc); BFS index order implies depth order
+__device__ __forceinline__ bool node_before(double s_a, int i_a, double s_b, int i_b) {
+    return s_a > s_b || (s_a == s_b && i_a < i_b);
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// a ranked candidate of the depth loop: key (Rk, tie) and its slot
+struct __align__(16) SurvKey {
+    double rk;
+    uint32_t tie;
+    uint32_t j;           // index of the child in T_{t-1}
+};
+// what a winner needs besides its key: cumulative score and the continuity
+// mask of its own children's context
+struct __align__(16) SurvAux {
+    double s;
+    uint32_t cm;
+    uint32_t pad;
+};
+// a frontier node as the next depth reads it: key, score, the continuity
+// mask of its children's context and its index in its own T list
+struct __align__(16) NodeRec {
+    double rk;
+    double s;
+    uint32_t cm;
+    uint32_t tidx;
+};
+
+template <typename T>
+__device__ __forceinline__ T* lds_at(unsigned char* base, int off) {
+    return reinterpret_cast<T*>(base + off);
+}
+
+// exclusive prefix sum over the workgroup (one value per thread); tmp holds kTreeWaves ints
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) tmp[wave] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < kTreeWaves; ++w) {
+        if (w < wave) before += tmp[w];
+        all += tmp[w];
+    }
+    __syncthreads();
+    *total = all;
+    return before + x - v;
+}
+
+// Steps 5 and 6 on a candidate tree of nb nodes held in LDS in BFS order
+// (tokens, parents as node indices, depths, cumulative scores).  `literal`
+// replays best-first one node at a time (scores may rise along a path);
+// otherwise S never rises along a path and the top-budget nodes by (S desc,
+// BFS index asc) are already closed under parents.
+struct EmitOut {
+    int32_t* n_nodes;
+    int32_t* tokens;
+    int32_t* parents;
+    int32_t* depths;
+    float* scores;
+    uint32_t* mask;
+    int budget;
+    int mask_words;
+};
+
+__device__ __forceinline__ void budget_and_emit(int nb, bool literal, int b, const int* n_tok, const int* n_par,
+                                                const int* n_dep, const double* n_s, int* n_new, int* n_out,
+                                                int* misc, const EmitOut& eo) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int budget = eo.budget;
+    // ---- 5. verification budget
+    int n_sel = nb;
+    if (nb <= budget) {
+        for (int i = tid; i < nb; i += kTreeThreads) {
+            n_new[i] = i;
+            n_out[i] = i;
+        }
+        __syncthreads();
+    } else if (!literal) {
+        // parent-closed top-budget by (S desc, BFS index asc)
+        const int per = (nb + kTreeThreads - 1) / kTreeThreads;
+        int flags = 0, cntl = 0;
+        for (int q = 0; q < per; ++q) {
+            const int i = tid * per + q;
+            if (i < nb) {
+                int r = 0;
+                const double si = n_s[i];
+                for (int j = 0; j < nb; ++j) r += node_before(n_s[j], j, si, i);
+                if (r < budget) {
+                    flags |= 1 << q;
+                    ++cntl;
+                }
+            }
+        }
+        int total;
+        int pos = block_exclusive_scan(cntl, misc + 16, &total);
+        for (int q = 0; q < per; ++q) {
+            const int i = tid * per + q;
+            if (i < nb) {
+                if (flags >> q & 1) {
+                    n_new[i] = pos;
+                    n_out[pos] = i;
+                    ++pos;
+                } else {
+                    n_new[i] = -1;
+                }
+            }
+        }
+        n_sel = total;
+        __syncthreads();
+    } else {
+        // best-first, literally: take the best available node budget times
+        for (int i = tid; i < nb; i += kTreeThreads) n_new[i] = (n_par[i] < 0) ? -2 : -3;  // -2 available, -3 waiting
+        __syncthreads();
+        if (wave == 0) {
+            for (int step = 0; step < budget; ++step) {
+                double bs = -INFINITY;
+                int bi = -1;
+                for (int i = lane; i < nb; i += 64)
+                    if (n_new[i] == -2 && (bi < 0 || node_before(n_s[i], i, bs, bi))) {
+                        bs = n_s[i];
+                        bi = i;
+                    }
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) {
+                    const double os = __shfl_xor(bs, off);
+                    const int oi = __shfl_xor(bi, off);
+                    if (oi >= 0 && (bi < 0 || node_before(os, oi, bs, bi))) {
+                        bs = os;
+                        bi = oi;
+                    }
+                }
+                if (bi < 0) break;                                // cannot happen: nb > budget
+                __builtin_amdgcn_wave_barrier();
+                if (lane == 0) n_new[bi] = -1;                    // taken (index assigned below)
+                __builtin_amdgcn_wave_barrier();
+                for (int i = lane; i < nb; i += 64)
+                    if (n_par[i] == bi) n_new[i] = -2;
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+        __syncthreads();
+        // taken nodes keep BFS order
+        const int per = (nb + kTreeThreads - 1) / kTreeThreads;
+        int cntl = 0;
+        for (int q = 0; q < per; ++q) {
+            const int i = tid * per + q;
+            if (i < nb && n_new[i] == -1) ++cntl;
+        }
+        int total;
+        int pos = block_exclusive_scan(cntl, misc + 16, &total);
+        __syncthreads();
+        for (int q = 0; q < per; ++q) {
+            const int i = tid * per + q;
+            if (i < nb) {
+                if (n_new[i] == -1) {
+                    n_new[i] = pos;
+                    n_out[pos] = i;
+                    ++pos;
+                } else {
+                    n_new[i] = -1;
+                }
+            }
+        }
+        n_sel = total;
+        __syncthreads();
+    }
+
+    // ---- 6. outputs in BFS order, parents remapped, ancestor mask
+    const int64_t ob = (int64_t)b * budget;
+    for (int o = tid; o < budget; o += kTreeThreads) {
+        if (o < n_sel) {
+            const int i = n_out[o];
+            eo.tokens[ob + o] = n_tok[i];
+            eo.parents[ob + o] = n_par[i] < 0 ? -1 : n_new[n_par[i]];
+            eo.depths[ob + o] = n_dep[i];
+            eo.scores[ob + o] = (float)n_s[i];
+        } else {
+            eo.tokens[ob + o] = -1;
+            eo.parents[ob + o] = -1;
+            eo.depths[ob + o] = 0;
+            eo.scores[ob + o] = -INFINITY;
+        }
+    }
+    const int words = eo.mask_words;
+    if (budget * words > kTreeThreads && words <= 8) {
+        // more (node, word) pairs than threads: one thread per node walks its
+        // ancestors once and sets their bits in all its words
+        for (int o = tid; o < budget; o += kTreeThreads) {
+            uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0, a4 = 0, a5 = 0, a6 = 0, a7 = 0;
+            if (o < n_sel) {
+                for (int i = n_out[o]; i >= 0; i = n_par[i]) {
+                    const int ni = n_new[i];
+                    const uint32_t bit = 1u << (ni & 31), wd = (uint32_t)ni >> 5;
+                    a0 |= wd == 0 ? bit : 0u;
+                    a1 |= wd == 1 ? bit : 0u;
+                    a2 |= wd == 2 ? bit : 0u;
+                    a3 |= wd == 3 ? bit : 0u;
+                    a4 |= wd == 4 ? bit : 0u;
+                    a5 |= wd == 5 ? bit : 0u;
+                    a6 |= wd == 6 ? bit : 0u;
+                    a7 |= wd == 7 ? bit : 0u;
+                }
+            }
+            uint32_t* row = eo.mask + (ob + o) * words;
+            row[0] = a0;
+            if (words > 1) row[1] = a1;
+            if (words > 2) row[2] = a2;
+            if (words > 3) row[3] = a3;
+            if (words > 4) row[4] = a4;
+            if (words > 5) row[5] = a5;
+            if (words > 6) row[6] = a6;
+            if (words > 7) row[7] = a7;
+        }
+    } else {
+        for (int e = tid; e < budget * words; e += kTreeThreads) {
+            const int o = e / words, w = e - o * words;
+            uint32_t bits = 0;
+            if (o < n_sel) {
+                for (int i = n_out[o]; i >= 0; i = n_par[i]) {
+                    const int ni = n_new[i];
+                    if ((ni >> 5) == w) bits |= 1u << (ni & 31);
+                }
+            }
+            eo.mask[ob * words + e] = bits;
+        }
+    }
+    if (tid == 0) eo.n_nodes[b] = n_sel;
+}
+
+// 1 if the survivor held SH lanes away within the 16-lane row (DPP
+// row_ror:SH of the (key low, key high, tie) words) ranks before (rk, tie).
+template <int SH>
+__device__ __forceinline__ int beats_rotated(uint32_t lo, uint32_t hi, uint32_t tie, double rk, uint32_t mytie) {
+    const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0x120 + SH, 0xF, 0xF, false);
+    const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, 0x120 + SH, 0xF, 0xF, false);
+    const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)tie, 0x120 + SH, 0xF, 0xF, false);
+    const double ork = __longlong_as_double((long long)(((uint64_t)h << 32) | l));
+    return (ork > rk) | ((ork == rk) & (t < mytie));
+}
+
+// Step 4 for one request whose per-row data (normalisers, top-k lists,
+// continuity masks and, in DARTree mode, parent-conditioned terms) are in
+// shared memory at plan P: the depth loop, run by wave 0 alone, leaving the
+// candidate tree (n_tok, n_par, n_dep, n_s in BFS order) in shared memory.
+// Every thread of the workgroup must call it; returns the number of nodes.
+template <int RM>
+__device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds, int d, int k, int W, int kind,
+                                          bool dartree) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    (void)tid;
+    const double* s_lse = lds_at<double>(lds, P.off_lse);
+    const int* s_ttok = lds_at<int>(lds, P.off_ttok);
+    const float* s_tx = lds_at<float>(lds, P.off_tx);
+    const uint32_t* s_vmask = lds_at<uint32_t>(lds, P.off_vmask);
+    const double* s_g = lds_at<double>(lds, P.off_g);
+    int* n_tok = lds_at<int>(lds, P.off_n_tok);
+    int* n_par = lds_at<int>(lds, P.off_n_par);
+    int* n_dep = lds_at<int>(lds, P.off_n_dep);
+    NodeRec* n_rec = lds_at<NodeRec>(lds, P.off_n_rec);
+    SurvKey* sv_key = lds_at<SurvKey>(lds, P.off_sv_key);
+    SurvAux* sv_aux = lds_at<SurvAux>(lds, P.off_sv_s);
+    double* n_s = lds_at<double>(lds, P.off_n_s);
+    int* misc = lds_at<int>(lds, P.off_misc);
+    // ---- 4. depth loop, run by wave 0 alone (wave-synchronous, no barriers).
+    //      Candidate slot r*64 + lane = parent_rank * k + child.  Every phase
+    //      issues its LDS reads together, so a depth costs a few LDS round
+    //      trips: (a) the candidates read the child's logit and token and
+    //      the parent's 32-byte frontier record; (b) the candidates that can
+    //      still win fetch the continuity mask of their own children's
+    //      context and are packed (with a full frontier only keys that reach
+    //      the smallest "first valid child" key of the W parents can be among
+    //      the top W: those W candidates are distinct); (c) ranks among the
+    //      survivors: up to 32 of them are compared all-pairs, each lane
+    //      taking a few rotations of a replicated copy and the replicas'
+    //      counts summed with lane shuffles; more are streamed sixteen at a
+    //      time.  Winners write their records in parallel.
+    int nb = 0;       // nodes in the candidate tree
+    if (wave == 0) {
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        int f = 1;        // frontier size (depth 0: the root)
+        int fbase = 0;    // BFS index of the first frontier node
+        const uint32_t root_mask = kind == DT_NGRAM_NONE ? 0xFFFFFFFFu : s_vmask[0];
+        const float inv_k = 1.0f / (float)k;
+        // per-depth constants, lane t-1 holding depth t's: normaliser and the
+        // mask of children with a finite logit
+        const double lse_l = lane < d ? s_lse[lane] : 0.0;
+        uint32_t live_l = 0;
+        if (lane < d)
+            for (int j = 0; j < k; ++j) live_l |= (uint32_t)(s_tx[lane * k + j] != -INFINITY) << j;
+        // a lane's candidate slots have fixed (parent rank, child) pairs
+        int cj[RM], cp[RM];
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            const int slot = r * 64 + lane;
+            const int sl = slot < kMaxCandidates ? slot : 0;
+            cp[r] = (int)(((float)sl + 0.5f) * inv_k);         // exact: slot < 2^11
+            cj[r] = sl - cp[r] * k;
+        }
+        for (int t = 1; t <= d; ++t) {
+            const int tk = (t - 1) * k;
+            const int m = f * k;
+            const double lse_t = readlane_d(lse_l, t - 1);
+            const uint32_t live = (uint32_t)__builtin_amdgcn_readlane((int)live_l, t - 1);
+            const bool next_ctx = kind != DT_NGRAM_NONE && t < d;
+            // (a) one batch of LDS reads for all rounds; indices are clamped so
+            //     every read is in bounds and no read waits on a branch
+            int ctok[RM];
+            float cx[RM];
+            u4 crec[RM];
+            u2 crec2[RM];
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                const int nd = (t > 1 && r * 64 + lane < m) ? fbase + cp[r] : 0;
+                cx[r] = s_tx[tk + cj[r]];
+                ctok[r] = s_ttok[tk + cj[r]];
+                crec[r] = *reinterpret_cast<const u4*>(&n_rec[nd]);
+                crec2[r] = *reinterpret_cast<const u2*>(&n_rec[nd].cm);
+            }
+            double krk[RM], ksc[RM];
+            uint32_t ktie[RM];
+            bool kok[RM];
+            int kgp[RM];
+            int nvalid = 0, nfirst = 0;
+            double firstmin = INFINITY;
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                const int slot = r * 64 + lane;
+                const int j = cj[r];
+                const bool root = t == 1;
+                const double prk = root ? 0.0 : __longlong_as_double(((long long)crec[r].y << 32) | crec[r].x);
+                const double ps = root ? 0.0 : __longlong_as_double(((long long)crec[r].w << 32) | crec[r].z);
+                const uint32_t cm = root ? root_mask : crec2[r].x;
+                kgp[r] = root ? 0 : (int)crec2[r].y;
+                const uint32_t rowv = cm & live;
+                const bool ok = slot < m && ((rowv >> j) & 1u);
+                const bool first = ok && j == __builtin_ctz(rowv);
+                const double g = (dartree && ok) ? s_g[(tk + kgp[r]) * k + j] : 0.0;
+                krk[r] = ok ? (prk + (double)cx[r]) + g : -INFINITY;
+                ksc[r] = ok ? (ps + ((double)cx[r] - lse_t)) + g : -INFINITY;
+                ktie[r] = ok ? (((uint32_t)ctok[r] << 6) | (uint32_t)cp[r]) : 0xFFFFFFFFu;
+                if (first) firstmin = min_d(firstmin, krk[r]);
+                kok[r] = ok;
+                nvalid += __popcll(__ballot(ok));
+                nfirst += __popcll(__ballot(first));
+            }
+            if (nvalid == 0) break;
+            const int keep = nvalid < W ? nvalid : W;
+            // (b) survivors, each with the continuity mask of its children's
+            //     context (read before the reduction, so the two overlap)
+            uint32_t kcm[RM];
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                kcm[r] = 0xFFFFFFFFu;
+                if (next_ctx) {
+                    const int ci = kok[r] ? ctx_index(kind, k, t + 1, t == 1 ? 0 : kgp[r], cj[r]) : 0;
+                    kcm[r] = s_vmask[ci];
+                }
+            }
+            // (the smallest first-valid key, rounded down to fp32: still a
+            // lower bound, and a one-word wave reduction)
+            double lb = nfirst >= W ? (double)wave_min_f32(__double2float_rd(firstmin)) : -INFINITY;
+            // With many candidates above that bound (no continuity filter, or
+            // a parent term that reorders a parent's children), tighten it:
+            // the W-th largest of the lanes' best keys, each rounded down to
+            // fp32, is reached by W distinct candidates, so it bounds the
+            // depth's W-th key from below too.  Found bit by bit with ballots
+            // over the order-preserving bits of the rounded values.
+            int nin = 0;
+#pragma unroll
+            for (int r = 0; r < RM; ++r) nin += __popcll(__ballot(kok[r] && krk[r] >= lb));
+            // (up to 16 survivors take the register-only ranking below)
+            if (nin > (W <= 16 ? 16 : 32)) {
+                double lm = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < RM; ++r)
+                    if (kok[r]) lm = max_d(lm, krk[r]);
+                const uint32_t u = ord_bits(__float_as_uint(__double2float_rd(lm) + 0.0f));
+                uint32_t th = 0;
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t c = th | (1u << bit);
+                    if (__popcll(__ballot(u >= c)) >= W) th = c;
+                }
+                lb = max_d(lb, (double)__uint_as_float(unord_bits(th)));
+            }
+            int ns = 0;
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                const bool in = kok[r] && krk[r] >= lb;
+                const unsigned long long bal = __ballot(in);
+                if (in) {
+                    const int e = ns + lanes_below(bal);
+                    sv_key[e] = SurvKey{krk[r], ktie[r], (uint32_t)cj[r]};
+                    sv_aux[e] = SurvAux{ksc[r], kcm[r], 0u};
+                }
+                ns += __popcll(bal);
+            }
+            // sentinels (Rk = -inf beats nothing) round the list up to a
+            // multiple of 32
+            const int ns32 = (ns + 31) & ~31;
+            if (lane < ns32 - ns) sv_key[ns + lane] = SurvKey{-INFINITY, 0xFFFFFFFFu, 0u};
+            __builtin_amdgcn_wave_barrier();
+            // (c) ranks
+            if (ns <= 16) {
+                // Four replicas of the survivor list, one per 16-lane row:
+                // lane (row r, i) holds survivor i and survivor (i + 4r) mod 16,
+                // rotates the latter by 1..4 lanes within the row (DPP
+                // row_ror), so the four rows together compare survivor i with
+                // every other one; the rows' counts are summed with the
+                // row-swapping permutes.  One round of shared-memory reads.
+                const int i = lane & 15, rep = lane >> 4;
+                const SurvKey me = sv_key[i];
+                const SurvKey ot = sv_key[(i + 4 * rep) & 15];
+                const SurvAux ax = sv_aux[i];
+                const uint32_t ot_lo = (uint32_t)__double_as_longlong(ot.rk);
+                const uint32_t ot_hi = (uint32_t)((uint64_t)__double_as_longlong(ot.rk) >> 32);
+                const int part = beats_rotated<1>(ot_lo, ot_hi, ot.tie, me.rk, me.tie) +
+                                 beats_rotated<2>(ot_lo, ot_hi, ot.tie, me.rk, me.tie) +
+                                 beats_rotated<3>(ot_lo, ot_hi, ot.tie, me.rk, me.tie) +
+                                 beats_rotated<4>(ot_lo, ot_hi, ot.tie, me.rk, me.tie);
+                const auto q16 = __builtin_amdgcn_permlane16_swap((uint32_t)part, (uint32_t)part, false, false);
+                const uint32_t pair = q16[0] + q16[1];                  // rows 0+1 | 2+3
+                const auto q32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
+                const int rank = (int)(q32[0] + q32[1]);
+                if (rep == 0 && i < ns && rank < keep) {
+                    const int nd = nb + rank;
+                    n_tok[nd] = (int)(me.tie >> 6);
+                    n_par[nd] = t == 1 ? -1 : fbase + (int)(me.tie & 63u);
+                    n_dep[nd] = t;
+                    n_s[nd] = ax.s;
+                    n_rec[nd] = NodeRec{me.rk, ax.s, ax.cm, me.j};
+                }
+            } else if (ns <= 32) {
+                // G lanes per replica, 64/G replicas; lane (rep, i) compares
+                // survivor i with survivors i+s (mod G), s = 1 + rep + u*64/G
+                const int G = ns <= 16 ? 16 : 32;
+                const int F = 64 / G;
+                const int i = lane & (G - 1), rep = lane / G;
+                const SurvKey me = sv_key[i];
+                const SurvAux ax = sv_aux[i];
+                int part = 0;
+                for (int s0 = 1 + rep; s0 < G; s0 += 4 * F) {
+                    u4 o[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int sh = s0 + u * F;
+                        o[u] = *reinterpret_cast<const u4*>(&sv_key[(i + (sh < G ? sh : 0)) & (G - 1)]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int sh = s0 + u * F;
+                        const double ork = __longlong_as_double(((long long)o[u].y << 32) | o[u].x);
+                        part += (sh < G) & ((ork > me.rk) | ((ork == me.rk) & (o[u].z < me.tie)));
+                    }
+                }
+                if (G == 16) {
+                    const auto q16 = __builtin_amdgcn_permlane16_swap((uint32_t)part, (uint32_t)part, false, false);
+                    part = (int)(q16[0] + q16[1]);
+                }
+                const auto q32 = __builtin_amdgcn_permlane32_swap((uint32_t)part, (uint32_t)part, false, false);
+                part = (int)(q32[0] + q32[1]);
+                if (rep == 0 && i < ns && part < keep) {
+                    const int nd = nb + part;
+                    n_tok[nd] = (int)(me.tie >> 6);
+                    n_par[nd] = t == 1 ? -1 : fbase + (int)(me.tie & 63u);
+                    n_dep[nd] = t;
+                    n_s[nd] = ax.s;
+                    n_rec[nd] = NodeRec{me.rk, ax.s, ax.cm, me.j};
+                }
+            } else {
+                // lane e holds survivor e (blocks of 64) and streams past all
+                for (int e0 = 0; e0 < ns; e0 += 64) {
+                    const int e = e0 + lane;
+                    const int ec = e < ns ? e : 0;
+                    const SurvKey me = sv_key[ec];
+                    const SurvAux ax = sv_aux[ec];
+                    int rank = 0;
+                    for (int q = 0; q < ns32; q += 16) {
+                        u4 o[16];
+#pragma unroll
+                        for (int u = 0; u < 16; ++u) o[u] = *reinterpret_cast<const u4*>(&sv_key[q + u]);
+#pragma unroll
+                        for (int u = 0; u < 16; ++u) {
+                            const double ork = __longlong_as_double(((long long)o[u].y << 32) | o[u].x);
+                            rank += (ork > me.rk) | ((ork == me.rk) & (o[u].z < me.tie));
+                        }
+                    }
+                    if (e < ns && rank < keep) {
+                        const int nd = nb + rank;
+                        n_tok[nd] = (int)(me.tie >> 6);
+                        n_par[nd] = t == 1 ? -1 : fbase + (int)(me.tie & 63u);
+                        n_dep[nd] = t;
+                        n_s[nd] = ax.s;
+                        n_rec[nd] = NodeRec{me.rk, ax.s, ax.cm, me.j};
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            fbase = nb;
+            nb += keep;
+            f = keep;
+        }
+        if (lane == 0) misc[0] = nb;
+    }
+    __syncthreads();
+    nb = misc[0];                                            // ordered by the barrier
+    return nb;
+}
+
+}  // namespace treedev
+}  // namespace dt

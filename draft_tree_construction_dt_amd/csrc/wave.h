@@ -11,14 +11,23 @@
 
 namespace dt {
 
+// (every step reads a lane of its own row, so no lane is out of bounds and
+// the moves need no initial value)
 __device__ __forceinline__ int dpp_step(int v, int ctrl) {
     switch (ctrl) {
-    case 0: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    case 1: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-    default: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); // row_mirror
+    case 0: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    case 1: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    case 2: return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    default: return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false); // row_mirror
     }
 }
+
+// min / max by compare and select: the operands are never NaN here, and the
+// library's fmin/fmax would first canonicalise both (two more instructions)
+__device__ __forceinline__ double min_d(double a, double b) { return b < a ? b : a; }
+__device__ __forceinline__ double max_d(double a, double b) { return b > a ? b : a; }
+__device__ __forceinline__ float min_f(float a, float b) { return b < a ? b : a; }
+__device__ __forceinline__ float max_f(float a, float b) { return b > a ? b : a; }
 
 __device__ __forceinline__ uint64_t dpp_step64(uint64_t v, int ctrl) {
     const uint32_t lo = (uint32_t)dpp_step((int)(uint32_t)v, ctrl);
@@ -34,36 +43,46 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
 
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) v = fmaxf(v, __int_as_float(dpp_step(__float_as_int(v), s)));
+    for (int s = 0; s < 4; ++s) v = max_f(v, __int_as_float(dpp_step(__float_as_int(v), s)));
     const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
     const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
     const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
     const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+    return max_f(max_f(a, b), max_f(c, d));
+}
+
+__device__ __forceinline__ float wave_min_f32(float v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v = min_f(v, __int_as_float(dpp_step(__float_as_int(v), s)));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return min_f(min_f(a, b), min_f(c, d));
 }
 
 __device__ __forceinline__ double wave_max_f64(double v) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        v = fmax(v, __longlong_as_double((long long)dpp_step64((uint64_t)__double_as_longlong(v), s)));
+        v = max_d(v, __longlong_as_double((long long)dpp_step64((uint64_t)__double_as_longlong(v), s)));
     const uint64_t u = (uint64_t)__double_as_longlong(v);
     const double a = __longlong_as_double((long long)readlane64(u, 0));
     const double b = __longlong_as_double((long long)readlane64(u, 16));
     const double c = __longlong_as_double((long long)readlane64(u, 32));
     const double d = __longlong_as_double((long long)readlane64(u, 48));
-    return fmax(fmax(a, b), fmax(c, d));
+    return max_d(max_d(a, b), max_d(c, d));
 }
 
 __device__ __forceinline__ double wave_min_f64(double v) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        v = fmin(v, __longlong_as_double((long long)dpp_step64((uint64_t)__double_as_longlong(v), s)));
+        v = min_d(v, __longlong_as_double((long long)dpp_step64((uint64_t)__double_as_longlong(v), s)));
     const uint64_t u = (uint64_t)__double_as_longlong(v);
     const double a = __longlong_as_double((long long)readlane64(u, 0));
     const double b = __longlong_as_double((long long)readlane64(u, 16));
     const double c = __longlong_as_double((long long)readlane64(u, 32));
     const double d = __longlong_as_double((long long)readlane64(u, 48));
-    return fmin(fmin(a, b), fmin(c, d));
+    return min_d(min_d(a, b), min_d(c, d));
 }
 
 __device__ __forceinline__ double wave_add_f64(double v) {
