@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 BATCH = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_traffic.json")
 SWEEP_SOURCES = [os.path.join(ROOT, "draft_tree_construction_dt_amd", "csrc", f)
-                 for f in ("sweep.hip", "common.h", "wave.h")]
+                 for f in ("sweep.hip", "sweep_dev.h", "common.h", "wave.h")]
 
 
 def parse():
@@ -384,6 +384,21 @@ def run_workload(args) -> None:
             "timing": "HIP events recorded by the library around the depth loop, one stream",
             "dtype": "bf16 MFMA for the screen (dense bf16 peak), fp64 exact rescoring of the survivors",
         }
+    if prob.mode == bd.DT_MODE_DARTREE:
+        # the parent-conditioned contraction g = E[parent] . F[child] on fp64
+        # matrix cores: per request 2 R k (1 + (d - 1) k) flops (the root row at
+        # depth 1, k parents after); its kernel (prep_kernel, which also merges
+        # rows) is not timed apart live, so the whole call's median bounds its
+        # duration and the fraction below is a lower bound
+        R = prob.E.shape[1]
+        flops = 2.0 * R * prob.k * (1 + (prob.d - 1) * prob.k) * cfg.B
+        full = {
+            "bound": "mfma", "kernel": "prep_kernel: G = E[parents] F[children]^T, fp64 MFMA 16x16x4",
+            "achieved": flops / med / 1e6, "peak": 78.6, "unit": "TFLOP/s",
+            "frac": flops / med / 1e6 / 78.6, "traffic": None, "algorithmic_flops_per_call": flops,
+            "timing": "the whole call's median (events) as the contraction's duration: a lower bound on the "
+                      "fraction; rocprofv3 MFMA counters are in profiles/",
+        }
     res = {
         "metric": METRIC, "workload": args.workload, "value": cfg.B / med * 1e6, "unit": "trees/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "B": cfg.B,
@@ -592,33 +607,6 @@ def main():
     b1_wall, _ = run(1, list(range(nreq)), K1, min(200, K1), nstream)
     b1_one, _ = run(1, list(range(nreq)), K1, min(200, K1), 1)
 
-    # ---- B = 1 replayed from HIP graphs: one captured call per request,
-    #      replayed round-robin back to back (the library enqueues kernels
-    #      only, so the whole call is capturable)
-    ng_graphs = min(64, nreq)
-    out_g = bd.alloc_tree_out(1, prob.budget, dev)
-    og = out_g._c()
-    keep_g, graphs = [], []
-    for r in range(ng_graphs):
-        q = params(1, r, None)
-        keep_g.append(q)
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            qc = q._c()
-            st = fn(logits[r].data_ptr(), ctypes.byref(ng_c), ctypes.byref(qc), ctypes.byref(og))
-            if st != 0:
-                raise bd.DtError(st, "dt_build_tree (capture)")
-        graphs.append(gr)
-    for gr in graphs:
-        gr.replay()
-    torch.cuda.synchronize()
-    tg = time.perf_counter()
-    for i in range(K1):
-        graphs[i % ng_graphs].replay()
-    torch.cuda.synchronize()
-    b1_graph = time.perf_counter() - tg
-    del graphs
-
     # ---- how many of each B=64 tree's nodes to verify (expected-speedup rule)
     qv = params(BATCH, 0, None)
     out_v = bd.alloc_tree_out(BATCH, prob.budget, dev)
@@ -683,9 +671,6 @@ def main():
             "us_per_tree": b1_one / K1 * 1e6,
             "trees_per_s": K1 / b1_one,
             "timing": "one stream, calls back to back: the latency of one request",
-            "graph_us_per_tree": b1_graph / K1 * 1e6,
-            "graph_timing": f"the same calls captured in {ng_graphs} HIP graphs (one per request) and replayed "
-                            "round-robin back to back on one stream",
             "trees_per_s_streams": K1 / b1_wall,
             "streams": nstream,
             "steps": K1,

@@ -674,8 +674,10 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
             int nin = 0;
 #pragma unroll
             for (int r = 0; r < RM; ++r) nin += __popcll(__ballot(kok[r] && krk[r] >= lb));
-            // (up to 16 survivors take the register-only ranking below)
-            if (nin > (W <= 16 ? 16 : 32)) {
+            // (up to 16 survivors take the register-only ranking below; with
+            // W above 12 the tightened bound rarely gets there, so it is
+            // tried only past 32)
+            if (nin > (W <= 12 ? 16 : 32)) {
                 double lm = -INFINITY;
 #pragma unroll
                 for (int r = 0; r < RM; ++r)
