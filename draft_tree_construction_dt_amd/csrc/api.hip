@@ -120,7 +120,7 @@ TreePlan plan_tree(const dt_params* p, int kind) {
     P.off_sv_key = take((P.max_cand + 32) * 16, 16);  // + a block of sentinels
     P.off_sv_s = take((P.max_cand + 32) * 16, 16);
     const int nn = P.max_nodes;
-    P.off_n_rec = take(nn * 32, 16);
+    P.off_n_rec = take((nn + 1) * 32, 16);      // + the root's record
     P.off_n_s = take(nn * 8, 8);
     P.off_n_tok = take(nn * 4, 4);
     P.off_n_par = take(nn * 4, 4);

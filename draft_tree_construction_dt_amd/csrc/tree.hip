@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
     }
 }
 
-template <int RM>
+template <int RM, bool DTREE, bool NG>
 __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const TreePlan& P = a.plan;
@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int d = a.d, k = a.k, W = a.W, budget = a.budget;
     const int kind = a.ng_kind;
-    const bool dartree = a.mode == DT_MODE_DARTREE;
+    constexpr bool dartree = DTREE;
 
     double* s_lse = lds_at<double>(lds, P.off_lse);
     int* s_ttok = lds_at<int>(lds, P.off_ttok);
@@ -207,9 +207,6 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     int* n_tok = lds_at<int>(lds, P.off_n_tok);
     int* n_par = lds_at<int>(lds, P.off_n_par);
     int* n_dep = lds_at<int>(lds, P.off_n_dep);
-    NodeRec* n_rec = lds_at<NodeRec>(lds, P.off_n_rec);
-    SurvKey* sv_key = lds_at<SurvKey>(lds, P.off_sv_key);
-    SurvAux* sv_aux = lds_at<SurvAux>(lds, P.off_sv_s);
     int* n_new = lds_at<int>(lds, P.off_n_new);
     int* n_out = lds_at<int>(lds, P.off_n_out);
     double* n_s = lds_at<double>(lds, P.off_n_s);
@@ -305,7 +302,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     }
     __syncthreads();
 
-    const int nb = depth_loop<RM>(P, lds, d, k, W, kind, dartree);
+    const int nb = depth_loop<RM, DTREE, NG>(P, lds, d, k, W, kind == DT_NGRAM_HASH_TRIGRAM);
     budget_and_emit(nb, dartree, b, n_tok, n_par, n_dep, n_s, n_new, n_out, misc,
                     EmitOut{a.n_nodes, a.tokens, a.parents, a.depths, a.scores, a.mask, budget, a.mask_words});
 }
@@ -363,15 +360,30 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int RM>
+static void launch_tree_rm(const TreeArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)a.B), block(kTreeThreads);
+    const size_t lds = (size_t)a.plan.total;
+    const bool dtree = a.mode == DT_MODE_DARTREE, ng = a.ng_kind != DT_NGRAM_NONE;
+    if (dtree && ng)
+        hipLaunchKernelGGL((tree_kernel<RM, true, true>), grid, block, lds, stream, a);
+    else if (dtree)
+        hipLaunchKernelGGL((tree_kernel<RM, true, false>), grid, block, lds, stream, a);
+    else if (ng)
+        hipLaunchKernelGGL((tree_kernel<RM, false, true>), grid, block, lds, stream, a);
+    else
+        hipLaunchKernelGGL((tree_kernel<RM, false, false>), grid, block, lds, stream, a);
+}
+
 hipError_t launch_tree(const TreeArgs& a, hipStream_t stream) {
     if (a.B <= 0) return hipSuccess;
     const int m = a.W * a.k;
     if (m <= 128)
-        hipLaunchKernelGGL(tree_kernel<2>, dim3((unsigned)a.B), dim3(kTreeThreads), (size_t)a.plan.total, stream, a);
+        launch_tree_rm<2>(a, stream);
     else if (m <= 256)
-        hipLaunchKernelGGL(tree_kernel<4>, dim3((unsigned)a.B), dim3(kTreeThreads), (size_t)a.plan.total, stream, a);
+        launch_tree_rm<4>(a, stream);
     else
-        hipLaunchKernelGGL(tree_kernel<16>, dim3((unsigned)a.B), dim3(kTreeThreads), (size_t)a.plan.total, stream, a);
+        launch_tree_rm<16>(a, stream);
     return hipGetLastError();
 }
 

@@ -314,14 +314,31 @@ struct __align__(16) SurvAux {
     uint32_t cm;
     uint32_t pad;
 };
-// a frontier node as the next depth reads it: key, score, the continuity
-// mask of its children's context and its index in its own T list
+// a node of the candidate tree: the next depth reads its key, score, the
+// continuity mask of its children's context and its index in its own T list
+// (the first 24 bytes); the output stage reads its token, parent and depth
 struct __align__(16) NodeRec {
     double rk;
     double s;
     uint32_t cm;
-    uint32_t tidx;
+    uint32_t tj;          // index in its own T list | depth << 8
+    int32_t tok;
+    int32_t par;          // BFS index of the parent, -1 at depth 1
 };
+
+// High word of the order-preserving 64-bit image of a double (sign bit
+// flipped for values >= +0, all bits inverted below): monotone in the
+// value, so the double whose image is (o, 0) is at most every value whose
+// high word is >= o.
+__device__ __forceinline__ uint32_t ord_hi(double x) {
+    const uint32_t h = (uint32_t)((uint64_t)__double_as_longlong(x) >> 32);
+    return h ^ ((uint32_t)((int32_t)h >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ double ord_hi_floor(uint32_t o) {
+    const uint32_t h = (o & 0x80000000u) ? (o ^ 0x80000000u) : ~o;
+    const uint32_t l = (o & 0x80000000u) ? 0u : 0xFFFFFFFFu;
+    return __longlong_as_double((long long)(((uint64_t)h << 32) | l));
+}
 
 template <typename T>
 __device__ __forceinline__ T* lds_at(unsigned char* base, int off) {
@@ -546,13 +563,14 @@ __device__ __forceinline__ int beats_rotated(uint32_t lo, uint32_t hi, uint32_t 
 // continuity masks and, in DARTree mode, parent-conditioned terms) are in
 // shared memory at plan P: the depth loop, run by wave 0 alone, leaving the
 // candidate tree (n_tok, n_par, n_dep, n_s in BFS order) in shared memory.
-// Every thread of the workgroup must call it; returns the number of nodes.
-template <int RM>
-__device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds, int d, int k, int W, int kind,
-                                          bool dartree) {
+// DTREE: the parent-conditioned term is added; NG: continuity masks apply
+// (trigram contexts when `trigram`, else bigram).  Every thread of the
+// workgroup must call it; returns the number of nodes.
+template <int RM, bool DTREE, bool NG>
+__device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds, int d, int k, int W,
+                                          bool trigram) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-    (void)tid;
     const double* s_lse = lds_at<double>(lds, P.off_lse);
     const int* s_ttok = lds_at<int>(lds, P.off_ttok);
     const float* s_tx = lds_at<float>(lds, P.off_tx);
@@ -566,26 +584,27 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
     SurvAux* sv_aux = lds_at<SurvAux>(lds, P.off_sv_s);
     double* n_s = lds_at<double>(lds, P.off_n_s);
     int* misc = lds_at<int>(lds, P.off_misc);
+    const int nn = P.max_nodes;                  // the root's record sits at n_rec[nn]
     // ---- 4. depth loop, run by wave 0 alone (wave-synchronous, no barriers).
-    //      Candidate slot r*64 + lane = parent_rank * k + child.  Every phase
-    //      issues its LDS reads together, so a depth costs a few LDS round
-    //      trips: (a) the candidates read the child's logit and token and
-    //      the parent's 32-byte frontier record; (b) the candidates that can
-    //      still win fetch the continuity mask of their own children's
-    //      context and are packed (with a full frontier only keys that reach
-    //      the smallest "first valid child" key of the W parents can be among
-    //      the top W: those W candidates are distinct); (c) ranks among the
-    //      survivors: up to 32 of them are compared all-pairs, each lane
-    //      taking a few rotations of a replicated copy and the replicas'
-    //      counts summed with lane shuffles; more are streamed sixteen at a
-    //      time.  Winners write their records in parallel.
+    //      Candidate slot r*64 + lane = parent_rank * k + child.  A depth
+    //      costs a few rounds of shared-memory reads: (a) every candidate
+    //      reads the child's logit and token and the parent's record, then
+    //      what depends on the parent's T index (the parent-conditioned term,
+    //      the continuity mask of its own children's context); (b) with a
+    //      full frontier only keys that reach the smallest "first valid
+    //      child" key of the W parents can be among the top W (those W
+    //      candidates are distinct), and those survivors are packed; (c) ranks
+    //      among the survivors: up to 32 of them are compared all-pairs, each
+    //      lane taking a few rotations of a replicated copy and the replicas'
+    //      counts summed with lane permutes; more are streamed sixteen at a
+    //      time.  Winners write their 32-byte records in parallel.
     int nb = 0;       // nodes in the candidate tree
     if (wave == 0) {
         typedef uint32_t u4 __attribute__((ext_vector_type(4)));
         typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        if (lane == 0) n_rec[nn] = NodeRec{0.0, 0.0, NG ? s_vmask[0] : 0xFFFFFFFFu, 0u, -1, -1};
         int f = 1;        // frontier size (depth 0: the root)
         int fbase = 0;    // BFS index of the first frontier node
-        const uint32_t root_mask = kind == DT_NGRAM_NONE ? 0xFFFFFFFFu : s_vmask[0];
         const float inv_k = 1.0f / (float)k;
         // per-depth constants, lane t-1 holding depth t's: normaliser and the
         // mask of children with a finite logit
@@ -595,105 +614,123 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
             for (int j = 0; j < k; ++j) live_l |= (uint32_t)(s_tx[lane * k + j] != -INFINITY) << j;
         // a lane's candidate slots have fixed (parent rank, child) pairs
         int cj[RM], cp[RM];
+        uint32_t below[RM];   // the children ranked before cj in T
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
             const int slot = r * 64 + lane;
             const int sl = slot < kMaxCandidates ? slot : 0;
             cp[r] = (int)(((float)sl + 0.5f) * inv_k);         // exact: slot < 2^11
             cj[r] = sl - cp[r] * k;
+            below[r] = (1u << cj[r]) - 1u;                     // cj < 32
         }
+        __builtin_amdgcn_wave_barrier();
         for (int t = 1; t <= d; ++t) {
             const int tk = (t - 1) * k;
             const int m = f * k;
+            const int rb = t == 1 ? nn : fbase;          // the parents' records
+            const int pbase = t == 1 ? -1 : fbase;       // parent index = pbase + parent rank
             const double lse_t = readlane_d(lse_l, t - 1);
             const uint32_t live = (uint32_t)__builtin_amdgcn_readlane((int)live_l, t - 1);
-            const bool next_ctx = kind != DT_NGRAM_NONE && t < d;
-            // (a) one batch of LDS reads for all rounds; indices are clamped so
-            //     every read is in bounds and no read waits on a branch
+            // context of a depth-t candidate's own children (depth t + 1):
+            // cbase + (parent's T index) * cstride + child index
+            const bool next_ctx = NG && t < d;
+            const int cbase = !trigram ? 1 + (t - 1) * k : (t == 1 ? 1 : 1 + k + (t - 2) * k * k);
+            const int cstride = (trigram && t > 1) ? k : 0;
+            // (a) one batch of reads for all rounds, then the reads that
+            //     depend on the parent's T index; indices are clamped so every
+            //     read is in bounds and none waits on a branch
             int ctok[RM];
             float cx[RM];
             u4 crec[RM];
             u2 crec2[RM];
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
-                const int nd = (t > 1 && r * 64 + lane < m) ? fbase + cp[r] : 0;
+                const int nd = r * 64 + lane < m ? rb + cp[r] : rb;
                 cx[r] = s_tx[tk + cj[r]];
                 ctok[r] = s_ttok[tk + cj[r]];
                 crec[r] = *reinterpret_cast<const u4*>(&n_rec[nd]);
                 crec2[r] = *reinterpret_cast<const u2*>(&n_rec[nd].cm);
             }
-            double krk[RM], ksc[RM];
-            uint32_t ktie[RM];
-            bool kok[RM];
-            int kgp[RM];
-            int nvalid = 0, nfirst = 0;
-            double firstmin = INFINITY;
+            double gv[RM];
+            uint32_t kcm[RM];
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
-                const int slot = r * 64 + lane;
-                const int j = cj[r];
-                const bool root = t == 1;
-                const double prk = root ? 0.0 : __longlong_as_double(((long long)crec[r].y << 32) | crec[r].x);
-                const double ps = root ? 0.0 : __longlong_as_double(((long long)crec[r].w << 32) | crec[r].z);
-                const uint32_t cm = root ? root_mask : crec2[r].x;
-                kgp[r] = root ? 0 : (int)crec2[r].y;
-                const uint32_t rowv = cm & live;
-                const bool ok = slot < m && ((rowv >> j) & 1u);
-                const bool first = ok && j == __builtin_ctz(rowv);
-                const double g = (dartree && ok) ? s_g[(tk + kgp[r]) * k + j] : 0.0;
-                krk[r] = ok ? (prk + (double)cx[r]) + g : -INFINITY;
-                ksc[r] = ok ? (ps + ((double)cx[r] - lse_t)) + g : -INFINITY;
+                const int kgp = (int)(crec2[r].y & 0xFFu);
+                gv[r] = DTREE ? s_g[(tk + kgp) * k + cj[r]] : 0.0;
+                if (NG) {
+                    const uint32_t v = s_vmask[next_ctx ? cbase + kgp * cstride + cj[r] : 0];
+                    kcm[r] = next_ctx ? v : 0xFFFFFFFFu;
+                } else {
+                    kcm[r] = 0xFFFFFFFFu;
+                }
+            }
+            double krk[RM], ksc[RM];
+            uint32_t ktie[RM];
+            int nvalid = 0, nfirst = 0;
+            uint32_t fmin = 0xFFFFFFFFu;    // smallest ordered high word of a first-valid key
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                const double prk = __longlong_as_double(((long long)crec[r].y << 32) | crec[r].x);
+                const double ps = __longlong_as_double(((long long)crec[r].w << 32) | crec[r].z);
+                const uint32_t rowv = NG ? (crec2[r].x & live) : live;
+                // single comparisons, so each ballot is one compare's mask:
+                // sel = the child's bit for a slot of a real parent, else 0
+                const uint32_t sel = r * 64 + lane < m ? 1u << cj[r] : 0u;
+                const bool ok = (rowv & sel) != 0u;
+                const bool first = (rowv & (sel | below[r])) == (sel ? sel : 0xFFFFFFFFu);
+                double kr = prk + (double)cx[r];
+                double ks = ps + ((double)cx[r] - lse_t);
+                if (DTREE) {
+                    kr += gv[r];
+                    ks += gv[r];
+                }
+                krk[r] = ok ? kr : -INFINITY;
+                ksc[r] = ok ? ks : -INFINITY;
                 ktie[r] = ok ? (((uint32_t)ctok[r] << 6) | (uint32_t)cp[r]) : 0xFFFFFFFFu;
-                if (first) firstmin = min_d(firstmin, krk[r]);
-                kok[r] = ok;
+                const uint32_t o = ord_hi(kr);
+                if (first && o < fmin) fmin = o;
                 nvalid += __popcll(__ballot(ok));
                 nfirst += __popcll(__ballot(first));
             }
             if (nvalid == 0) break;
             const int keep = nvalid < W ? nvalid : W;
-            // (b) survivors, each with the continuity mask of its children's
-            //     context (read before the reduction, so the two overlap)
-            uint32_t kcm[RM];
-#pragma unroll
-            for (int r = 0; r < RM; ++r) {
-                kcm[r] = 0xFFFFFFFFu;
-                if (next_ctx) {
-                    const int ci = kok[r] ? ctx_index(kind, k, t + 1, t == 1 ? 0 : kgp[r], cj[r]) : 0;
-                    kcm[r] = s_vmask[ci];
-                }
-            }
-            // (the smallest first-valid key, rounded down to fp32: still a
-            // lower bound, and a one-word wave reduction)
-            double lb = nfirst >= W ? (double)wave_min_f32(__double2float_rd(firstmin)) : -INFINITY;
+            // (b) the bound: the W first-valid keys are distinct candidates,
+            //     so the depth's W-th key is at least the smallest of them
+            //     (taken on the high words of their ordered images)
+            // (every valid key is finite, so a bound of -DBL_MAX admits all of
+            // them and no invalid one)
+            double lb = -1.7976931348623157e308;
+            if (nfirst >= W) lb = ord_hi_floor(wave_min_u32(fmin));
             // With many candidates above that bound (no continuity filter, or
             // a parent term that reorders a parent's children), tighten it:
-            // the W-th largest of the lanes' best keys, each rounded down to
-            // fp32, is reached by W distinct candidates, so it bounds the
-            // depth's W-th key from below too.  Found bit by bit with ballots
-            // over the order-preserving bits of the rounded values.
+            // the W-th largest of the lanes' best keys, taken on the same high
+            // words, is reached by W distinct candidates, so it bounds the
+            // depth's W-th key from below too.  Found bit by bit with ballots.
             int nin = 0;
 #pragma unroll
-            for (int r = 0; r < RM; ++r) nin += __popcll(__ballot(kok[r] && krk[r] >= lb));
+            for (int r = 0; r < RM; ++r) nin += __popcll(__ballot(krk[r] >= lb));
             // (up to 16 survivors take the register-only ranking below; with
             // W above 12 the tightened bound rarely gets there, so it is
             // tried only past 32)
             if (nin > (W <= 12 ? 16 : 32)) {
-                double lm = -INFINITY;
+                // (a lane without a valid candidate has -inf, whose high word
+                // 0x000FFFFF is below every finite key's; a threshold that low
+                // maps to a NaN, which leaves lb as it is)
+                double lm = krk[0];
 #pragma unroll
-                for (int r = 0; r < RM; ++r)
-                    if (kok[r]) lm = max_d(lm, krk[r]);
-                const uint32_t u = ord_bits(__float_as_uint(__double2float_rd(lm) + 0.0f));
+                for (int r = 1; r < RM; ++r) lm = max_d(lm, krk[r]);
+                const uint32_t u = ord_hi(lm);
                 uint32_t th = 0;
                 for (int bit = 31; bit >= 0; --bit) {
                     const uint32_t c = th | (1u << bit);
                     if (__popcll(__ballot(u >= c)) >= W) th = c;
                 }
-                lb = max_d(lb, (double)__uint_as_float(unord_bits(th)));
+                lb = max_d(lb, ord_hi_floor(th));
             }
             int ns = 0;
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
-                const bool in = kok[r] && krk[r] >= lb;
+                const bool in = krk[r] >= lb;
                 const unsigned long long bal = __ballot(in);
                 if (in) {
                     const int e = ns + lanes_below(bal);
@@ -707,6 +744,7 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
             const int ns32 = (ns + 31) & ~31;
             if (lane < ns32 - ns) sv_key[ns + lane] = SurvKey{-INFINITY, 0xFFFFFFFFu, 0u};
             __builtin_amdgcn_wave_barrier();
+            const uint32_t tdep = (uint32_t)t << 8;
             // (c) ranks
             if (ns <= 16) {
                 // Four replicas of the survivor list, one per 16-lane row:
@@ -729,19 +767,13 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
                 const uint32_t pair = q16[0] + q16[1];                  // rows 0+1 | 2+3
                 const auto q32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
                 const int rank = (int)(q32[0] + q32[1]);
-                if (rep == 0 && i < ns && rank < keep) {
-                    const int nd = nb + rank;
-                    n_tok[nd] = (int)(me.tie >> 6);
-                    n_par[nd] = t == 1 ? -1 : fbase + (int)(me.tie & 63u);
-                    n_dep[nd] = t;
-                    n_s[nd] = ax.s;
-                    n_rec[nd] = NodeRec{me.rk, ax.s, ax.cm, me.j};
-                }
+                if (rep == 0 && i < ns && rank < keep)
+                    n_rec[nb + rank] = NodeRec{me.rk, ax.s, ax.cm, me.j | tdep, (int)(me.tie >> 6),
+                                               pbase + (int)(me.tie & 63u)};
             } else if (ns <= 32) {
-                // G lanes per replica, 64/G replicas; lane (rep, i) compares
-                // survivor i with survivors i+s (mod G), s = 1 + rep + u*64/G
-                const int G = ns <= 16 ? 16 : 32;
-                const int F = 64 / G;
+                // 32 lanes per replica, two replicas; lane (rep, i) compares
+                // survivor i with survivors i+s (mod 32), s = 1 + rep + 2u
+                constexpr int G = 32, F = 2;
                 const int i = lane & (G - 1), rep = lane / G;
                 const SurvKey me = sv_key[i];
                 const SurvAux ax = sv_aux[i];
@@ -760,20 +792,11 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
                         part += (sh < G) & ((ork > me.rk) | ((ork == me.rk) & (o[u].z < me.tie)));
                     }
                 }
-                if (G == 16) {
-                    const auto q16 = __builtin_amdgcn_permlane16_swap((uint32_t)part, (uint32_t)part, false, false);
-                    part = (int)(q16[0] + q16[1]);
-                }
                 const auto q32 = __builtin_amdgcn_permlane32_swap((uint32_t)part, (uint32_t)part, false, false);
                 part = (int)(q32[0] + q32[1]);
-                if (rep == 0 && i < ns && part < keep) {
-                    const int nd = nb + part;
-                    n_tok[nd] = (int)(me.tie >> 6);
-                    n_par[nd] = t == 1 ? -1 : fbase + (int)(me.tie & 63u);
-                    n_dep[nd] = t;
-                    n_s[nd] = ax.s;
-                    n_rec[nd] = NodeRec{me.rk, ax.s, ax.cm, me.j};
-                }
+                if (rep == 0 && i < ns && part < keep)
+                    n_rec[nb + part] = NodeRec{me.rk, ax.s, ax.cm, me.j | tdep, (int)(me.tie >> 6),
+                                               pbase + (int)(me.tie & 63u)};
             } else {
                 // lane e holds survivor e (blocks of 64) and streams past all
                 for (int e0 = 0; e0 < ns; e0 += 64) {
@@ -792,14 +815,9 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
                             rank += (ork > me.rk) | ((ork == me.rk) & (o[u].z < me.tie));
                         }
                     }
-                    if (e < ns && rank < keep) {
-                        const int nd = nb + rank;
-                        n_tok[nd] = (int)(me.tie >> 6);
-                        n_par[nd] = t == 1 ? -1 : fbase + (int)(me.tie & 63u);
-                        n_dep[nd] = t;
-                        n_s[nd] = ax.s;
-                        n_rec[nd] = NodeRec{me.rk, ax.s, ax.cm, me.j};
-                    }
+                    if (e < ns && rank < keep)
+                        n_rec[nb + rank] = NodeRec{me.rk, ax.s, ax.cm, me.j | tdep, (int)(me.tie >> 6),
+                                                   pbase + (int)(me.tie & 63u)};
                 }
             }
             __builtin_amdgcn_wave_barrier();
@@ -811,6 +829,15 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
     }
     __syncthreads();
     nb = misc[0];                                            // ordered by the barrier
+    // the output stage's per-node arrays
+    for (int i = tid; i < nb; i += kTreeThreads) {
+        const NodeRec rec = n_rec[i];
+        n_tok[i] = rec.tok;
+        n_par[i] = rec.par;
+        n_dep[i] = (int)(rec.tj >> 8);
+        n_s[i] = rec.s;
+    }
+    __syncthreads();
     return nb;
 }
 

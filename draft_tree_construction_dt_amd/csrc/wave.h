@@ -122,6 +122,21 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
     return d < r ? d : r;
 }
 
+// minimum over the wave, left in every lane's register: the row butterfly,
+// then the two row-swapping permutes of gfx950 (rows r and r^1, then r and
+// r^2), so no value goes through a scalar register
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t o = (uint32_t)dpp_step((int)v, s);
+        v = o < v ? o : v;
+    }
+    const auto q16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = q16[0] < q16[1] ? q16[0] : q16[1];
+    const auto q32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return q32[0] < q32[1] ? q32[0] : q32[1];
+}
+
 __device__ __forceinline__ int wave_add_i32(int v) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) v += dpp_step(v, s);
