@@ -552,9 +552,11 @@ __device__ __forceinline__ void budget_and_emit(int nb, bool literal, int b, con
 // row_ror:SH of the (key low, key high, tie) words) ranks before (rk, tie).
 template <int SH>
 __device__ __forceinline__ int beats_rotated(uint32_t lo, uint32_t hi, uint32_t tie, double rk, uint32_t mytie) {
-    const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0x120 + SH, 0xF, 0xF, false);
-    const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, 0x120 + SH, 0xF, 0xF, false);
-    const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)tie, 0x120 + SH, 0xF, 0xF, false);
+    // (a rotation inside the row reads a lane of the row for every lane, so
+    // the moves need no initial value)
+    const uint32_t l = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, 0x120 + SH, 0xF, 0xF, false);
+    const uint32_t h = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, 0x120 + SH, 0xF, 0xF, false);
+    const uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)tie, 0x120 + SH, 0xF, 0xF, false);
     const double ork = __longlong_as_double((long long)(((uint64_t)h << 32) | l));
     return (ork > rk) | ((ork == rk) & (t < mytie));
 }
@@ -757,6 +759,9 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
                 const SurvKey me = sv_key[i];
                 const SurvKey ot = sv_key[(i + 4 * rep) & 15];
                 const SurvAux ax = sv_aux[i];
+                // (keeps the winners' fields in the same round of reads
+                // instead of a second one after the ranks)
+                asm volatile("" ::"v"(ax.s), "v"(ax.cm), "v"(me.j));
                 const uint32_t ot_lo = (uint32_t)__double_as_longlong(ot.rk);
                 const uint32_t ot_hi = (uint32_t)((uint64_t)__double_as_longlong(ot.rk) >> 32);
                 const int part = beats_rotated<1>(ot_lo, ot_hi, ot.tie, me.rk, me.tie) +
@@ -777,20 +782,20 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
                 const int i = lane & (G - 1), rep = lane / G;
                 const SurvKey me = sv_key[i];
                 const SurvAux ax = sv_aux[i];
+                // all sixteen reads in the same round as the lane's own
+                u4 o[G / F];
+#pragma unroll
+                for (int u = 0; u < G / F; ++u) {
+                    const int sh = 1 + rep + u * F;
+                    o[u] = *reinterpret_cast<const u4*>(&sv_key[(i + (sh < G ? sh : 0)) & (G - 1)]);
+                }
+                asm volatile("" ::"v"(ax.s), "v"(ax.cm), "v"(me.j));
                 int part = 0;
-                for (int s0 = 1 + rep; s0 < G; s0 += 4 * F) {
-                    u4 o[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int sh = s0 + u * F;
-                        o[u] = *reinterpret_cast<const u4*>(&sv_key[(i + (sh < G ? sh : 0)) & (G - 1)]);
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int sh = s0 + u * F;
-                        const double ork = __longlong_as_double(((long long)o[u].y << 32) | o[u].x);
-                        part += (sh < G) & ((ork > me.rk) | ((ork == me.rk) & (o[u].z < me.tie)));
-                    }
+                for (int u = 0; u < G / F; ++u) {
+                    const int sh = 1 + rep + u * F;
+                    const double ork = __longlong_as_double(((long long)o[u].y << 32) | o[u].x);
+                    part += (sh < G) & ((ork > me.rk) | ((ork == me.rk) & (o[u].z < me.tie)));
                 }
                 const auto q32 = __builtin_amdgcn_permlane32_swap((uint32_t)part, (uint32_t)part, false, false);
                 part = (int)(q32[0] + q32[1]);
