@@ -179,6 +179,7 @@ struct NGramUpdateArgs {
 constexpr int kVocabReqPerWave = 2;                       // requests a wave owns
 constexpr int kVocabReqPerGroup = kVocabReqPerWave * kWaves;
 constexpr int kVocabCap = 320;                            // per-(wave, request) candidate buffer
+constexpr int kVocabGroupBlocks = 10;                     // 16-token blocks whose logits load together
 constexpr int kVocabChunk = 128;                          // least vocabulary columns per workgroup
 constexpr int kVocabGroups = 768;                         // workgroups a depth aims for (three per CU)
 constexpr int kFullMaxW = 16;                             // one 16-row MFMA tile per request

@@ -58,14 +58,14 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_m, cons
     }
 
     // normaliser: max and rescaled sum over the lists, log in fp64
-    const float M = wave_max_f32(fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3])));
+    const float M = wave_max_f32_all(max_f(max_f(mc[0], mc[1]), max_f(mc[2], mc[3])));
     double sum = 0.0;
     if (M != -INFINITY) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if (mc[q] != -INFINITY) sum += sc[q] * (double)__builtin_amdgcn_exp2f((mc[q] - M) * 1.4426950408889634f);
     }
-    sum = wave_add_f64(sum);
+    sum = wave_add_f64_all(sum);
     if (lane == 0) {
         // the true normaliser is >= the row max; clamp the rounding of a sum
         // whose largest term is 1 so that every log-probability stays <= 0
@@ -91,9 +91,9 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_m, cons
             }
         }
     }
-    bk = wave_max_u64(bk);
-    bq = wave_min_u64(bq);
-    nq = wave_add_i32(nq);
+    bk = wave_max_u64_all(bk);
+    bq = wave_min_u64_all(bq);
+    nq = wave_add_i32_all(nq);
     unsigned long long th = bk;
     if (nq * q >= k && bq > th) th = bq;
     int ns = 0;

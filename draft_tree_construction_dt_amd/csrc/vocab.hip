@@ -28,7 +28,12 @@
 //                    fp64 summed k = 0..R-1 over the fp32 E and F (fp32 x
 //                    fp32 products are exact in fp64, so the sum is the
 //                    oracle's bit for bit), and the chunk's exact top-W is
-//                    written out.
+//                    written out.  Before any product, a block of 16 tokens
+//                    is skipped when no token in it can reach the bound
+//                    even with the largest parent term Cauchy-Schwarz
+//                    allows (|g(p, v)| <= |E_p| |F_v|); the logits and F
+//                    norms this test needs are loaded for many blocks at
+//                    once, and only the blocks that pass load F rows.
 //  frontier_kernel - one workgroup per request: merges the chunks' sorted
 //                    lists (the largest W-th entry of any list bounds the
 //                    frontier's W-th key from below, so only entries above it
@@ -137,12 +142,26 @@ __device__ uint32_t wave_kth_key32(const uint32_t (&key)[4], int kth) {
 
 // fp32 screen thresholds of the four output rows a lane holds: a candidate
 // whose fp64 interval reaches lam has (x + acc) + e32 >= thr; the slack
-// covers the fp64 roundings of the key (the screen may only pass more)
-__device__ __forceinline__ void row_thresholds(float (&thr)[4], double lam, const double* rk) {
+// covers the fp64 roundings of the key (the screen may only pass more).
+// Rows past the frontier get +inf, so nothing passes there; the screen
+// takes a missing or -inf logit as NaN, which passes nothing either.
+__device__ __forceinline__ void row_thresholds(float (&thr)[4], double lam, const double* rk, int nrow, int kq) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        thr[i] = lam == -INFINITY ? -INFINITY
-                                  : __double2float_rd((lam - rk[i]) - 0x1p-40 * (fabs(lam) + fabs(rk[i])));
+        thr[i] = 4 * kq + i >= nrow ? INFINITY
+                 : lam == -INFINITY ? -INFINITY
+                                    : __double2float_rd((lam - rk[i]) - 0x1p-40 * (fabs(lam) + fabs(rk[i])));
+}
+
+// Block skip.  |g(p, v)| <= |E_p| |F_v| (Cauchy-Schwarz), so no frontier
+// node gives token v a key above rkmax + x_v + Emax |F_v|; a block of tokens
+// none of which reaches lam that way holds no candidate and is skipped
+// before its products.  The fp32 test x + Emax' |F_v| >= ts takes Emax' a
+// little above the largest |E_p| (covering the fp32 norms) and ts rounded
+// down with room for the fp64 roundings of the keys and of the test.
+__device__ __forceinline__ float skip_threshold(double lam, double rkmax) {
+    return lam == -INFINITY ? -INFINITY
+                            : __double2float_rd((lam - rkmax) - 0x1p-30 * (fabs(lam) + fabs(rkmax)) - 0x1p-100);
 }
 
 // exact key of one candidate, summed like the oracle: k = 0 .. R-1 (the rows
@@ -336,21 +355,48 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
     float A[kVocabReqPerWave][KS];
     uint32_t Ab[kVocabReqPerWave][KS / 2];
     float eb[kVocabReqPerWave][4];
+    float emax[kVocabReqPerWave];   // a little above the largest |E_p| of the frontier
     int nf[kVocabReqPerWave], bq[kVocabReqPerWave];
+    // The first group of logits and F norms (they do not depend on the
+    // frontier), then every frontier read of both requests, are issued
+    // before anything waits on them; indices are clamped so each read is in
+    // bounds.
+    const int64_t rowoff = (int64_t)(a.t - 1) * a.V;
+    int64_t xrow[kVocabReqPerWave];
+#pragma unroll
+    for (int j = 0; j < kVocabReqPerWave; ++j) {
+        bq[j] = rg * kVocabReqPerGroup + wave + kWaves * j;
+        xrow[j] = (int64_t)(bq[j] < a.B ? bq[j] : 0) * a.d * a.V + rowoff;
+    }
+    constexpr int G = kVocabGroupBlocks;
+    float gn[G];
+    uint32_t gx[G][kVocabReqPerWave];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const int cl = q * 16 + m;
+        const int v = col0 + (cl < ncol ? cl : ncol - 1);
+        gn[q] = a.fnorm[v];
+#pragma unroll
+        for (int j = 0; j < kVocabReqPerWave; ++j) gx[q][j] = load_raw<DT>(a.logits, xrow[j] + v);
+    }
+    int nraw[kVocabReqPerWave], traw[kVocabReqPerWave];
+    double rraw[kVocabReqPerWave], seedv[kVocabReqPerWave];
+#pragma unroll
+    for (int j = 0; j < kVocabReqPerWave; ++j) {
+        const int bc = bq[j] < a.B ? bq[j] : 0;
+        const int64_t fi = (int64_t)bc * W + (m < W ? m : 0);
+        nraw[j] = a.t == 1 ? 1 : a.f_n[bc];
+        traw[j] = a.t == 1 ? a.ctx[2 * bc + 1] : a.f_tok[fi];
+        rraw[j] = a.t == 1 ? 0.0 : a.f_rk[fi];
+        seedv[j] = a.seed[bc];
+    }
 #pragma unroll
     for (int j = 0; j < kVocabReqPerWave; ++j) {
         const int slot = wave * kVocabReqPerWave + j;
-        const int b = rg * kVocabReqPerGroup + wave + kWaves * j;
-        bq[j] = b;
-        int n = 0;
-        if (b < a.B) n = a.t == 1 ? 1 : a.f_n[b];
-        nf[j] = __builtin_amdgcn_readfirstlane(n);
-        int tokm = -1;
-        double rkm = 0.0;
-        if (m < nf[j]) {
-            tokm = a.t == 1 ? a.ctx[2 * b + 1] : a.f_tok[(int64_t)b * W + m];
-            rkm = a.t == 1 ? 0.0 : a.f_rk[(int64_t)b * W + m];
-        }
+        const int b = bq[j];
+        nf[j] = __builtin_amdgcn_readfirstlane(b < a.B ? nraw[j] : 0);
+        const int tokm = m < nf[j] ? traw[j] : -1;
+        const double rkm = m < nf[j] ? rraw[j] : 0.0;
         // a root token outside the vocabulary adds no parent term (E row 0)
         const bool has_e = (unsigned)tokm < (unsigned)a.V;
         if (kq == 0) {
@@ -383,135 +429,161 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
             const int r = 4 * kq + i;
             eb[j][i] = 0x1.2p-7f * sqrtf(__shfl(ne, r));
         }
+        emax[j] = sqrtf(wave_max_f32_all(ne)) * (1.0f + 0x1p-14f);
     }
     __builtin_amdgcn_wave_barrier();
+    double rkmax[kVocabReqPerWave];
+#pragma unroll
+    for (int j = 0; j < kVocabReqPerWave; ++j) {
+        const int slot = wave * kVocabReqPerWave + j;
+        rkmax[j] = wave_max_f64(m < nf[j] ? L.rk[slot][m] : -INFINITY);
+    }
 
     double lam[kVocabReqPerWave], lst[kVocabReqPerWave];
     int cnt[kVocabReqPerWave];
-    float thr[kVocabReqPerWave][4];
+    float thr[kVocabReqPerWave][4], ts[kVocabReqPerWave];
 #pragma unroll
     for (int j = 0; j < kVocabReqPerWave; ++j) {
-        lam[j] = nf[j] > 0 ? a.seed[bq[j]] : -INFINITY;                // exact keys of real candidates
+        lam[j] = nf[j] > 0 ? seedv[j] : -INFINITY;                     // exact keys of real candidates
         lst[j] = -INFINITY;
         cnt[j] = 0;
-        row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq]);
+        row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq], nf[j], kq);
+        ts[j] = skip_threshold(lam[j], rkmax[j]);
     }
-    const int64_t rowoff = (int64_t)(a.t - 1) * a.V;
-    int64_t xrow[kVocabReqPerWave];
-#pragma unroll
-    for (int j = 0; j < kVocabReqPerWave; ++j) xrow[j] = nf[j] > 0 ? (int64_t)bq[j] * a.d * a.V + rowoff : 0;
     const int nblk = (ncol + 15) >> 4;
 
-    // block cb + 1's F rows, norms and logits are loaded while block cb is
-    // scored; every load reads a valid address (the last column for the
-    // padding of a ragged chunk) and validity is applied where the block is
-    // used
-    uint32_t fc[KS / 2];
-    float nc;
-    uint32_t xc[kVocabReqPerWave];
-    {
-        const int v = col0 + (m < ncol ? m : ncol - 1);
-        nc = a.fnorm[v];
-        load_fbf<KS>(a.Fbf, v, kq, fc);
+    // The blocks' logits and F norms are loaded a group of kVocabGroupBlocks
+    // blocks at a time (one memory round trip per group) and the bound above
+    // marks the blocks that can hold a candidate of each request; only those
+    // load their F rows and run the products and the screen.  Every load
+    // reads a valid address (the last column for the padding of a ragged
+    // chunk) and validity is applied where the block is used.
+    for (int g0 = 0; g0 < nblk; g0 += G) {
+        if (g0 > 0) {                                                   // (the first group is loaded)
 #pragma unroll
-        for (int j = 0; j < kVocabReqPerWave; ++j) xc[j] = load_raw<DT>(a.logits, xrow[j] + v);
-    }
-    for (int cb = 0; cb < nblk; ++cb) {
-        const int cl = cb * 16 + m;
-        const bool vv = cl < ncol;
-        const int v = col0 + (vv ? cl : ncol - 1);
-        // the next block's loads are issued on every iteration (the last one
-        // re-reads the chunk's last column): a conditional load would make
-        // the compiler wait for them before this block's products
-        uint32_t fn[KS / 2];
-        uint32_t xn[kVocabReqPerWave];
-        const int cln = cl + 16;
-        const int vn = col0 + (cln < ncol ? cln : ncol - 1);
-        const float nn = a.fnorm[vn];
-        load_fbf<KS>(a.Fbf, vn, kq, fn);
+            for (int q = 0; q < G; ++q) {
+                const int cl = (g0 + q) * 16 + m;
+                const int v = col0 + (cl < ncol ? cl : ncol - 1);
+                gn[q] = a.fnorm[v];
 #pragma unroll
-        for (int j = 0; j < kVocabReqPerWave; ++j) xn[j] = load_raw<DT>(a.logits, xrow[j] + vn);
-        const float nfv = nc;
-        v4f acc[kVocabReqPerWave];
-#pragma unroll
-        for (int j = 0; j < kVocabReqPerWave; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < kVocabReqPerWave; ++j) acc[j] = mfma_bf16<KS>(Ab[j], fc, acc[j]);
+                for (int j = 0; j < kVocabReqPerWave; ++j) gx[q][j] = load_raw<DT>(a.logits, xrow[j] + v);
+            }
+        }
+        uint32_t livem[kVocabReqPerWave], anyl = 0u;      // bit q: block g0 + q (wave-uniform)
 #pragma unroll
         for (int j = 0; j < kVocabReqPerWave; ++j) {
-            if (nf[j] == 0) continue;                                   // wave-uniform
-            const int slot = wave * kVocabReqPerWave + j;
-            const float x = vv ? raw_logit<DT>(xc[j]) : -INFINITY;
-            bool ok[4], pf[4];
-            bool anyp = false;
+            livem[j] = 0u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ok[i] = (4 * kq + i < nf[j]) && x != -INFINITY;
-                const float sx = x + acc[j][i];
-                const float e32 = fmaf(eb[j][i], nfv, fabsf(sx) * 0x1p-22f + 0x1p-100f);
-                pf[i] = ok[i] && sx + e32 >= thr[j][i];
-                anyp |= pf[i];
+            for (int q = 0; q < G; ++q) {
+                const int cl = (g0 + q) * 16 + m;
+                const float xr = raw_logit<DT>(gx[q][j]);
+                const float x = (cl < ncol && xr != -INFINITY) ? xr : __builtin_nanf("");
+                const float w = fmaf(emax[j], gn[q], x);
+                const bool hit = __ballot(w + fabsf(w) * 0x1p-20f >= ts[j]) != 0ull;
+                livem[j] |= (hit && g0 + q < nblk && nf[j] > 0) ? 1u << q : 0u;
             }
-            if (lam[j] == -INFINITY) {
-                // seed the bound: the W-th largest lower end of this tile,
-                // rounded down to fp32
-                uint32_t key[4];
-                int nv = 0;
+            anyl |= livem[j];
+        }
+        while (anyl != 0u) {
+            const int q = __builtin_ctz(anyl);
+            anyl &= anyl - 1u;
+            const int cb = g0 + q;
+            const int cl = cb * 16 + m;
+            const bool vv = cl < ncol;
+            const int v = col0 + (vv ? cl : ncol - 1);
+            uint32_t fc[KS / 2];
+            load_fbf<KS>(a.Fbf, v, kq, fc);
+            const float nfv = a.fnorm[v];
+            float xs[kVocabReqPerWave];
+            bool live[kVocabReqPerWave];
+#pragma unroll
+            for (int j = 0; j < kVocabReqPerWave; ++j) {
+                const float xr = raw_logit<DT>(load_raw<DT>(a.logits, xrow[j] + v));
+                xs[j] = (vv && xr != -INFINITY) ? xr : __builtin_nanf("");
+                live[j] = (livem[j] >> q) & 1u;
+            }
+            v4f acc[kVocabReqPerWave];
+#pragma unroll
+            for (int j = 0; j < kVocabReqPerWave; ++j) {
+                acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+                if (live[j]) acc[j] = mfma_bf16<KS>(Ab[j], fc, acc[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < kVocabReqPerWave; ++j) {
+                if (!live[j]) continue;                                     // wave-uniform
+                const int slot = wave * kVocabReqPerWave + j;
+                const float x = xs[j];
+                // (branch-free: the thresholds reject rows past the frontier, and
+                // a NaN logit every comparison)
+                bool pf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float sx = x + acc[j][i];
+                    const float e32 = fmaf(eb[j][i], nfv, fmaf(fabsf(sx), 0x1p-22f, 0x1p-100f));
+                    pf[i] = sx + e32 >= thr[j][i];
+                }
+                const bool anyp = (pf[0] | pf[1]) | (pf[2] | pf[3]);
+                if (lam[j] == -INFINITY) {
+                    bool ok[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ok[i] = (4 * kq + i < nf[j]) && x == x;
+                    // seed the bound: the W-th largest lower end of this tile,
+                    // rounded down to fp32
+                    uint32_t key[4];
+                    int nv = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const double ak = (L.rk[slot][4 * kq + i] + (double)x) + (double)acc[j][i];
+                        const float e = eb[j][i] * nfv + fabsf((float)ak) * 0x1p-44f + 0x1p-100f;
+                        key[i] = ok[i] ? ord_bits(__float_as_uint(__double2float_rd(ak - (double)e))) : 0u;
+                        nv += __popcll(__ballot(ok[i]));
+                    }
+                    if (nv >= W) {
+                        lam[j] = (double)__uint_as_float(unord_bits(wave_kth_key32(key, W)));
+                        row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq], nf[j], kq);
+                        ts[j] = skip_threshold(lam[j], rkmax[j]);
+                    }
+                }
+                if (__ballot(anyp) == 0) continue;                          // nothing reaches the bound
+                int base = cnt[j];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const double ak = (L.rk[slot][4 * kq + i] + (double)x) + (double)acc[j][i];
                     const float e = eb[j][i] * nfv + fabsf((float)ak) * 0x1p-44f + 0x1p-100f;
-                    key[i] = ok[i] ? ord_bits(__float_as_uint(__double2float_rd(ak - (double)e))) : 0u;
-                    nv += __popcll(__ballot(ok[i]));
+                    const bool pass = pf[i] && ak + (double)e >= lam[j];
+                    unsigned long long bm = __ballot(pass);
+                    if (pass) {
+                        const int pos = base + lanes_below(bm);
+                        L.ak[slot][pos] = ak;
+                        L.e[slot][pos] = e;
+                        L.id[slot][pos] = ((uint32_t)v << 4) | (uint32_t)(4 * kq + i);
+                    }
+                    base += __popcll(bm);
+                    // the bound follows the W-th largest lower end inserted
+                    const double lo = ak - (double)e;
+                    while (bm) {
+                        const int src = __builtin_ctzll(bm);
+                        bm &= bm - 1;
+                        top_insert(lst[j], readlane_d(lo, src), W, lane);
+                    }
                 }
-                if (nv >= W) {
-                    lam[j] = (double)__uint_as_float(unord_bits(wave_kth_key32(key, W)));
-                    row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq]);
-                }
-            }
-            if (__ballot(anyp) == 0) continue;                          // nothing reaches the bound
-            int base = cnt[j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const double ak = (L.rk[slot][4 * kq + i] + (double)x) + (double)acc[j][i];
-                const float e = eb[j][i] * nfv + fabsf((float)ak) * 0x1p-44f + 0x1p-100f;
-                const bool pass = pf[i] && ak + (double)e >= lam[j];
-                unsigned long long bm = __ballot(pass);
-                if (pass) {
-                    const int pos = base + lanes_below(bm);
-                    L.ak[slot][pos] = ak;
-                    L.e[slot][pos] = e;
-                    L.id[slot][pos] = ((uint32_t)v << 4) | (uint32_t)(4 * kq + i);
-                }
-                base += __popcll(bm);
-                // the bound follows the W-th largest lower end inserted
-                const double lo = ak - (double)e;
-                while (bm) {
-                    const int src = __builtin_ctzll(bm);
-                    bm &= bm - 1;
-                    top_insert(lst[j], readlane_d(lo, src), W, lane);
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
-            cnt[j] = base;
-            const double lw = readlane_d(lst[j], W - 1);
-            if (lw > lam[j]) lam[j] = lw;
-            if (cnt[j] > kVocabCap - 256) {
-                // room for the next tile; if intervals still overlap too much
-                // (ties), settle the order exactly
-                compact(L, slot, cnt[j], lam[j], lane);
+                __builtin_amdgcn_wave_barrier();
+                cnt[j] = base;
+                const double lw = readlane_d(lst[j], W - 1);
+                if (lw > lam[j]) lam[j] = lw;
                 if (cnt[j] > kVocabCap - 256) {
-                    lam[j] = fmax(lam[j], finalize<DT, R>(L, slot, cnt[j], W, lane, a, bq[j], nullptr));
-                    lst[j] = lane < cnt[j] ? L.ak[slot][lane < kVocabCap ? lane : 0] : -INFINITY;
+                    // room for the next tile; if intervals still overlap too much
+                    // (ties), settle the order exactly
+                    compact(L, slot, cnt[j], lam[j], lane);
+                    if (cnt[j] > kVocabCap - 256) {
+                        lam[j] = fmax(lam[j], finalize<DT, R>(L, slot, cnt[j], W, lane, a, bq[j], nullptr));
+                        lst[j] = lane < cnt[j] ? L.ak[slot][lane < kVocabCap ? lane : 0] : -INFINITY;
+                    }
                 }
+                row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq], nf[j], kq);
+                ts[j] = skip_threshold(lam[j], rkmax[j]);
             }
-            row_thresholds(thr[j], lam[j], &L.rk[wave * kVocabReqPerWave + j][4 * kq]);
         }
-#pragma unroll
-        for (int s = 0; s < KS / 2; ++s) fc[s] = fn[s];
-#pragma unroll
-        for (int j = 0; j < kVocabReqPerWave; ++j) xc[j] = xn[j];
-        nc = nn;
     }
 
     // ---- the chunk's exact top-W per request

@@ -137,6 +137,91 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     return q32[0] < q32[1] ? q32[0] : q32[1];
 }
 
+// The same reductions with the result left in every lane's register: the
+// row butterfly, then the two row-swapping permutes (rows r and r^1, then r
+// and r^2).  Each permute pairs one row's partial with its partner's in the
+// same order in both rows, so every lane ends with the same value.
+__device__ __forceinline__ uint32_t swap_rows16(uint32_t v, uint32_t* other) {
+    const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    *other = q[1];
+    return q[0];
+}
+__device__ __forceinline__ uint32_t swap_rows32(uint32_t v, uint32_t* other) {
+    const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    *other = q[1];
+    return q[0];
+}
+
+__device__ __forceinline__ float wave_max_f32_all(float v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v = max_f(v, __int_as_float(dpp_step(__float_as_int(v), s)));
+    uint32_t o;
+    float a = __uint_as_float(swap_rows16(__float_as_uint(v), &o));
+    v = max_f(a, __uint_as_float(o));
+    a = __uint_as_float(swap_rows32(__float_as_uint(v), &o));
+    return max_f(a, __uint_as_float(o));
+}
+
+// 64-bit values move as two words
+__device__ __forceinline__ uint64_t swap_rows16_64(uint64_t v, uint64_t* other) {
+    uint32_t ol, oh;
+    const uint32_t l = swap_rows16((uint32_t)v, &ol), h = swap_rows16((uint32_t)(v >> 32), &oh);
+    *other = ((uint64_t)oh << 32) | ol;
+    return ((uint64_t)h << 32) | l;
+}
+__device__ __forceinline__ uint64_t swap_rows32_64(uint64_t v, uint64_t* other) {
+    uint32_t ol, oh;
+    const uint32_t l = swap_rows32((uint32_t)v, &ol), h = swap_rows32((uint32_t)(v >> 32), &oh);
+    *other = ((uint64_t)oh << 32) | ol;
+    return ((uint64_t)h << 32) | l;
+}
+
+__device__ __forceinline__ double wave_add_f64_all(double v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v += __longlong_as_double((long long)dpp_step64((uint64_t)__double_as_longlong(v), s));
+    uint64_t o;
+    double a = __longlong_as_double((long long)swap_rows16_64((uint64_t)__double_as_longlong(v), &o));
+    v = a + __longlong_as_double((long long)o);
+    a = __longlong_as_double((long long)swap_rows32_64((uint64_t)__double_as_longlong(v), &o));
+    return a + __longlong_as_double((long long)o);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64_all(uint64_t v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint64_t o = dpp_step64(v, s);
+        v = o > v ? o : v;
+    }
+    uint64_t o;
+    uint64_t a = swap_rows16_64(v, &o);
+    v = o > a ? o : a;
+    a = swap_rows32_64(v, &o);
+    return o > a ? o : a;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64_all(uint64_t v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint64_t o = dpp_step64(v, s);
+        v = o < v ? o : v;
+    }
+    uint64_t o;
+    uint64_t a = swap_rows16_64(v, &o);
+    v = o < a ? o : a;
+    a = swap_rows32_64(v, &o);
+    return o < a ? o : a;
+}
+
+__device__ __forceinline__ int wave_add_i32_all(int v) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v += dpp_step(v, s);
+    uint32_t o;
+    uint32_t a = swap_rows16((uint32_t)v, &o);
+    v = (int)(a + o);
+    a = swap_rows32((uint32_t)v, &o);
+    return (int)(a + o);
+}
+
 __device__ __forceinline__ int wave_add_i32(int v) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) v += dpp_step(v, s);
