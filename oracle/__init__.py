@@ -9,8 +9,9 @@ The arithmetic lives in ``oracle.c`` (plain C, double precision, full sorts);
 this module only marshals arguments.  What it computes and the readings it
 takes are stated in ``oracle.h``.  Parity status: every function here is
 pinned by ``tests/test_oracle_*.py`` (closed forms, library routines, brute
-force over all paths, textbook special cases, the DARTree sketch and a
-hand-derived worked example under ``tests/golden/``).
+force over all paths, textbook special cases, per-depth top-W checks that
+rescore every candidate from the logits, and a hand-derived worked example
+under ``tests/golden/``).
 """
 
 from __future__ import annotations

@@ -31,7 +31,7 @@
  *  - the budget counts draft nodes (root excluded);
  *  - full-vocabulary DARTree mode (ORACLE_MODE_DARTREE_FULL): the drafter
  *    proposes W tokens for every frontier node (DARTree page, "Tree
- *    Construction"; its sketch asks for width proposals per path) from that
+ *    Construction": W proposals per frontier node) from that
  *    node's own parent-conditioned distribution over the whole vocabulary,
  *    x[v] + E[parent_tok] . F[v]; a node's proposals are its W best tokens
  *    under the candidate order (Rk desc, token asc), and the frontier is then
