@@ -94,6 +94,8 @@ WorkspacePlan plan_workspace(const dt_params* p, const SweepPlan& s) {
     w.off_fnorm = take(full ? (int64_t)p->V * 4 : 0);
     w.off_fbf = take(full ? (int64_t)p->V * p->R * 2 : 0);
     w.off_seed = take(full ? B * 8 : 0);
+    w.off_cmp_n = take(full ? B * 4 : 0);
+    w.off_cmp = take(full ? B * kFrontCap * (int64_t)sizeof(VocabEntry) : 0);
     w.total = (size_t)round_up(off, 256);
     return w;
 }
@@ -280,12 +282,16 @@ static dt_status build_full(const void* logits, const dt_params* p, const SweepP
     va.f_n = (const int32_t*)(ws + w.off_f_n);
     va.part = (VocabEntry*)(ws + w.off_part);
     va.seed = (const double*)(ws + w.off_seed);
+    va.cmp_n = (int32_t*)(ws + w.off_cmp_n);
+    va.cmp = (VocabEntry*)(ws + w.off_cmp);
     FrontierArgs fa{};
     fa.B = p->B;
     fa.d = p->d;
     fa.W = p->W;
     fa.C2 = w.C2;
     fa.part = va.part;
+    fa.cmp_n = va.cmp_n;
+    fa.cmp = va.cmp;
     fa.lse = ma.lse;
     fa.f_tok = (int32_t*)(ws + w.off_f_tok);
     fa.f_rk = (double*)(ws + w.off_f_rk);

@@ -75,7 +75,7 @@ struct SweepPlan {
 struct WorkspacePlan {
     size_t off_m, off_s, off_keys, off_lse, off_ttok, off_tx, off_vmask, off_g;
     size_t off_f_tok, off_f_rk, off_f_s, off_f_node, off_f_n, off_n_tree;
-    size_t off_nd_tok, off_nd_par, off_nd_dep, off_nd_s, off_part, off_fnorm, off_fbf, off_seed;
+    size_t off_nd_tok, off_nd_par, off_nd_dep, off_nd_s, off_part, off_fnorm, off_fbf, off_seed, off_cmp_n, off_cmp;
     size_t total;
     int n_ctx_cap;      // contexts per request the vmask area holds (the trigram count)
     int vchunk, C2;     // full-vocabulary mode: columns per chunk and chunk count
@@ -195,6 +195,11 @@ struct VocabEntry {
     uint32_t pad[2];
 };
 
+// Each request's non-empty chunk lists of a depth, appended by the
+// vocabulary kernel (count cmp_n[b], entries cmp[b][0 .. kFrontCap)), so the
+// frontier kernel reads what was found in one round instead of every list
+constexpr int kFrontCap = 1024;
+
 struct VocabArgs {
     int B, V, d, W, R, t, dtype;
     int vchunk, C2;
@@ -209,11 +214,15 @@ struct VocabArgs {
     const int32_t* f_n;
     const double* seed;            // [B] a lower bound for this depth's W-th key (-inf = none)
     VocabEntry* part;
+    int32_t* cmp_n;                // [B] entries appended this depth
+    VocabEntry* cmp;               // [B][kFrontCap]
 };
 
 struct FrontierArgs {
     int B, V, d, W, t, C2, k, R;
     const VocabEntry* part;
+    int32_t* cmp_n;                // [B] read, then cleared for the next depth
+    const VocabEntry* cmp;         // [B][kFrontCap]
     const double* lse;
     const int32_t* ttok;           // [B*d][k] each row's top-k tokens
     const float* tx;               // [B*d][k] their logits

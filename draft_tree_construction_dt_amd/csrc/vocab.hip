@@ -255,7 +255,7 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
 // set, the list is also written there (W entries, empties padded).
 template <int DT, int R>
 __device__ double finalize(VocabLds& L, int slot, int& cnt, int W, int lane, const VocabArgs& a, int b,
-                           VocabEntry* out) {
+                           VocabEntry* out, VocabEntry* out2 = nullptr) {
     const int n = cnt;
     double K[kOwn], G[kOwn];
     float X[kOwn];
@@ -319,6 +319,7 @@ __device__ double finalize(VocabLds& L, int slot, int& cnt, int W, int lane, con
                 ve.pad[0] = rank[r] == 0 ? (uint32_t)(n < W ? n : W) : 0u;   // entry 0: the list's length
                 ve.pad[1] = 0u;
                 out[rank[r]] = ve;
+                if (out2) out2[rank[r]] = ve;
             }
             if (rank[r] == W - 1) lam = K[r];
         }
@@ -594,7 +595,18 @@ __global__ void __launch_bounds__(kThreads, 3) vocab_kernel(VocabArgs a) {
         const int slot = wave * kVocabReqPerWave + j;
         VocabEntry* out = a.part + ((int64_t)b * a.C2 + c) * W;
         if (cnt[j] > W) compact(L, slot, cnt[j], lam[j], lane);
-        finalize<DT, R>(L, slot, cnt[j], W, lane, a, b, out);
+        // a non-empty list is also appended to the request's compact list
+        // (a slot range taken with one atomic; past the capacity the frontier
+        // kernel falls back to the per-chunk lists)
+        const int kept = cnt[j] < W ? cnt[j] : W;
+        VocabEntry* out2 = nullptr;
+        if (kept > 0) {
+            int pos = 0;
+            if (lane == 0) pos = atomicAdd(&a.cmp_n[b], kept);
+            pos = __builtin_amdgcn_readfirstlane(pos);
+            if (pos + kept <= kFrontCap) out2 = a.cmp + (int64_t)b * kFrontCap + pos;
+        }
+        finalize<DT, R>(L, slot, cnt[j], W, lane, a, b, out, out2);
     }
 }
 
@@ -730,13 +742,15 @@ __global__ void __launch_bounds__(64) seed1_kernel(FrontierArgs a, const int32_t
     float A[KS];
     load_erow<KS>(a, (lane & 15) < 1 ? tok : -1, lane >> 4, A);
     const double s = seed_bound<KS>(a, sd, 1, A, &rk0, lane);
-    if (lane == 0) a.seed[b] = s;
+    if (lane == 0) {
+        a.seed[b] = s;
+        a.cmp_n[b] = 0;                                            // depth 1's compact list starts empty
+    }
 }
 
 // ---------------------------------------------------------------------------
 // frontier merge: one workgroup per request
 // ---------------------------------------------------------------------------
-constexpr int kFrontCap = 1024;
 constexpr int kHeadsPerLane = kMaxVocabChunks / 64;
 
 __device__ __forceinline__ bool entry_before(double ka, uint32_t ta, double kb, uint32_t tb) {
@@ -776,70 +790,43 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
     if (a.t < a.d) seed_side<KS>(a, b * a.d + a.t, lane, sd);
     const double lse_t = a.lse[(int64_t)b * a.d + (a.t - 1)];
 
-    // 1. list heads with their lengths
-    double hk[kHeadsPerLane];
-    int hc[kHeadsPerLane];
-#pragma unroll
-    for (int q = 0; q < kHeadsPerLane; ++q) {
-        const int c = lane + 64 * q;
-        hk[q] = c < C2 ? lists[(int64_t)c * W].rk : -INFINITY;
-        hc[q] = c < C2 ? (int)lists[(int64_t)c * W].pad[0] : 0;
-    }
-    int mine = 0;
-#pragma unroll
-    for (int q = 0; q < kHeadsPerLane; ++q) mine += hc[q];
-    const int total = wave_add_i32(mine);
+    // 1. the compact list of this depth's entries (its count and the first 64
+    //    entries in one round), then the count cleared for the next depth
+    const int ncmp = __builtin_amdgcn_readfirstlane(a.cmp_n[b]);
+    const VocabEntry* cl = a.cmp + (int64_t)b * kFrontCap;
+    const VocabEntry e0 = cl[lane];                                      // (in bounds: kFrontCap >= 64)
+    if (lane == 0 && ncmp >= 0) a.cmp_n[b] = 0;                        // (after the read: depends on it)
 
     int n = 0;
-    if (total <= kFrontCap) {
-        // 2a. every listed entry: the non-empty lists in chunk order, their
-        //     offsets, then 64 entries per round with all lanes loading
-        int nq = 0;
-#pragma unroll
-        for (int q = 0; q < kHeadsPerLane; ++q) {
-            const bool ne = hc[q] > 0;
-            const unsigned long long mq = __ballot(ne);
-            if (ne) s_q[nq + lanes_below(mq)] = (lane + 64 * q) | (hc[q] << 16);
-            nq += __popcll(mq);
+    double hk[kHeadsPerLane];
+    if (ncmp <= kFrontCap) {
+        // 2a. every entry found (usually a few dozen)
+        if (lane < ncmp) {
+            s_k[lane] = e0.rk;
+            s_t[lane] = e0.tie;
+            s_g[lane] = e0.g;
+            s_x[lane] = e0.x;
+            s_src[lane] = lane;
         }
-        __syncthreads();
-        // offsets of the lists' entries: an exclusive scan of their lengths,
-        // 64 lists per round
-        int run = 0;
-        for (int i0 = 0; i0 < nq; i0 += 64) {
-            const int i = i0 + lane;
-            const int len = i < nq ? s_q[i] >> 16 : 0;
-            int x = len;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o);
-                if (lane >= o) x += y;
-            }
-            if (i < nq) s_off[i] = run + x - len;
-            run += __shfl(x, 63);
-        }
-        if (lane == 0) s_off[nq] = run;
-        __syncthreads();
-        for (int it = lane; it < total; it += 64) {
-            int lo = 0, hi = nq - 1;                                    // the list holding item it
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_off[mid] <= it) lo = mid;
-                else hi = mid - 1;
-            }
-            const int idx = (s_q[lo] & 0xFFFF) * W + (it - s_off[lo]);
-            const VocabEntry e = lists[idx];
+        for (int it = 64 + lane; it < ncmp; it += 64) {
+            const VocabEntry e = cl[it];
             s_k[it] = e.rk;
             s_t[it] = e.tie;
             s_g[it] = e.g;
             s_x[it] = e.x;
             s_src[it] = it;
         }
-        n = total;
+        n = ncmp;
     } else {
-        // 2b. long lists: the W-th largest head bounds the frontier's W-th
-        //     key from below (W distinct entries reach it); read the entries
-        //     of the lists whose head reaches it
+        // 2b. more entries than the compact list holds: the W-th largest of
+        //     the chunk lists' heads bounds the frontier's W-th key from below
+        //     (W distinct entries reach it); read the entries of the lists
+        //     whose head reaches it
+#pragma unroll
+        for (int q = 0; q < kHeadsPerLane; ++q) {
+            const int c = lane + 64 * q;
+            hk[q] = c < C2 ? lists[(int64_t)c * W].rk : -INFINITY;
+        }
         uint32_t taken = 0;
         double bound = -INFINITY;
         int found = 0;
