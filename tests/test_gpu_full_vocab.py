@@ -73,6 +73,20 @@ def test_massive_ties(device, oracle_lib, seed):
     _parity(p, device, oracle_lib, f"ties{seed}")
 
 
+def test_massive_ties_overflow_the_compact_list(device, oracle_lib):
+    """Thousands of exactly tied candidates at a large vocabulary: every
+    vocabulary chunk keeps a full list of W, more entries than the
+    per-request compact list holds (313 chunks x 16 > 1024), so the frontier
+    falls back to the chunk lists' heads and, with every head tied, to taking
+    the best W one at a time."""
+    rng = np.random.default_rng(31)
+    p = synth.random_problem(rng, B=2, V=40000, d=3, k=16, W=16, budget=40, integer_logits=True,
+                             mode=MODE_DARTREE_FULL, R=16)
+    p.E[:] = 0
+    p.F[:] = 0
+    _parity(p, device, oracle_lib, "ties-overflow")
+
+
 def test_ties_in_logits_with_embeddings(device, oracle_lib):
     rng = np.random.default_rng(77)
     p = synth.random_problem(rng, B=2, V=1500, d=4, k=8, W=12, budget=30, integer_logits=True,
