@@ -20,8 +20,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTreeThreads = 256;      // tree kernel: four wave64s per request
 constexpr int kTreeWaves = kTreeThreads / 64;
 constexpr int kPrepRows = 3;           // rows a prep workgroup merges: children, parents, grandparents
-constexpr int kPrepThreads = 512;      // prep workgroup: eight waves
-constexpr int kPrepContexts = kPrepThreads / 4;  // trigram contexts per prep workgroup (one per lane quad)
+constexpr int kPrepContexts = 64;      // trigram contexts per prep workgroup (one per lane quad)
 constexpr int kMiscInts = 32;          // tree-kernel counters (0..3) and scan scratch (16..31)
 constexpr int kTreeLdsLimit = 160 * 1024;
 constexpr int kMergeKeysPerRow = 256;  // C * 4 * k bound: per-wave merge scratch

@@ -1,6 +1,6 @@
 // Tree construction: two kernels after the vocabulary sweep.
 //
-// prep_kernel -- one 512-thread workgroup per (request, depth t) [and slice
+// prep_kernel -- one 256-thread workgroup per (request, depth t) [and slice
 // of that depth's contexts], so the latency-bound random reads of the N-gram
 // table and of E/F are spread over many compute units instead of queueing in
 // one:
@@ -41,7 +41,7 @@ using namespace treedev;
 // ---------------------------------------------------------------------------
 // prep: rows, continuity and parent-conditioned terms of one depth
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrepArgs a) {
+__global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
     __shared__ unsigned long long s_scratch[kPrepRows][kMergeKeysPerRow + 8];
     __shared__ int s_tok[kPrepRows][kMaxK];
     __shared__ float s_x[kPrepRows][kMaxK];
@@ -65,7 +65,7 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrepArgs a) {
     if (wave < rows) {
         const int64_t row = (int64_t)b * d + (t - 1 - wave);
         merge_row(a.part_m, a.part_s, a.part_keys, row, a.L, k, s_scratch[wave], lane, &s_lse[wave],
-                  s_tok[wave], s_x[wave], wave == 0);                // rows t-2, t-3: tokens only
+                  s_tok[wave], s_x[wave]);
         if (wave == 0 && split == 0) {                       // row t-1 is written once
             if (lane < k) {
                 a.ttok[row * k + lane] = s_tok[0][lane];
@@ -94,7 +94,7 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrepArgs a) {
         // children of depth t by token (the trigram and CSR rows list
         // successors by token), then one lane quad per context
         if (kind != DT_NGRAM_DENSE_BIGRAM) {
-            for (int i = tid; i < kChildSlots; i += kPrepThreads) s_ctok[i] = -1;
+            for (int i = tid; i < kChildSlots; i += kThreads) s_ctok[i] = -1;
             __syncthreads();
             if (tid < k) {
                 const int tok = s_tok[0][tid];
@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrepArgs a) {
         uint32_t live = 0;
         for (int j = 0; j < k; ++j) live |= (uint32_t)(s_x[0][j] != -INFINITY) << j;
         const int g = tid & 3;
-        for (int c0 = lo; c0 < hi; c0 += kPrepThreads / 4) {
+        for (int c0 = lo; c0 < hi; c0 += kThreads / 4) {
             const int c = c0 + (tid >> 2);
             const bool active = c < hi;
             uint32_t m;
@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrepArgs a) {
         const int tk = (k + 15) >> 4;
         const int kp = t == 1 ? 1 : k;
         const int tiles = ((kp + 15) >> 4) * tk;
-        for (int tile = wave; tile < tiles; tile += kPrepThreads / 64) {
+        for (int tile = wave; tile < tiles; tile += kThreads / 64) {
             const int ti = tile / tk, tj = tile - ti * tk;
             const int i = ti * 16 + (lane & 15), j = tj * 16 + (lane & 15), grp = lane >> 4;
             int ptok = i < kp ? (t == 1 ? ctx1 : s_tok[1][i]) : -1;
@@ -356,7 +356,7 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
     if (a.B <= 0) return hipSuccess;
     const int64_t grid = (int64_t)a.B * a.d * a.nsplit;
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(kPrepThreads), 0, stream, a);
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

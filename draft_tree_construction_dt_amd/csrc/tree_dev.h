@@ -36,7 +36,7 @@ __device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
 __device__ __forceinline__ void merge_row(const float* __restrict__ part_m, const double* __restrict__ part_s,
                           const unsigned long long* __restrict__ part_keys, int64_t row, int L, int k,
                           unsigned long long* scratch, int lane, double* lse_out, int* tok_out,
-                          float* val_out, bool need_lse = true) {
+                          float* val_out) {
     const float* pm = part_m + row * L;
     const double* ps = part_s + row * L;
     const unsigned long long* keys = part_keys + row * (int64_t)L * k;
@@ -47,8 +47,8 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_m, cons
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int c = lane + 64 * q;
-        mc[q] = (need_lse && c < L) ? pm[c] : -INFINITY;
-        sc[q] = (need_lse && c < L) ? ps[c] : 0.0;
+        mc[q] = c < L ? pm[c] : -INFINITY;
+        sc[q] = c < L ? ps[c] : 0.0;
     }
     unsigned long long kv[4];
 #pragma unroll
@@ -57,23 +57,20 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_m, cons
         kv[q] = e < n ? keys[e] : 0ull;
     }
 
-    // normaliser: max and rescaled sum over the lists, log in fp64 (only
-    // where the caller needs it: a row merged for its tokens alone skips it)
-    if (need_lse) {
-        const float M = wave_max_f32_all(max_f(max_f(mc[0], mc[1]), max_f(mc[2], mc[3])));
-        double sum = 0.0;
-        if (M != -INFINITY) {
+    // normaliser: max and rescaled sum over the lists, log in fp64
+    const float M = wave_max_f32_all(max_f(max_f(mc[0], mc[1]), max_f(mc[2], mc[3])));
+    double sum = 0.0;
+    if (M != -INFINITY) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (mc[q] != -INFINITY) sum += sc[q] * (double)__builtin_amdgcn_exp2f((mc[q] - M) * 1.4426950408889634f);
-        }
-        sum = wave_add_f64_all(sum);
-        if (lane == 0) {
-            // the true normaliser is >= the row max; clamp the rounding of a
-            // sum whose largest term is 1 so that every log-probability stays <= 0
-            const double l = log(sum);
-            *lse_out = (M == -INFINITY) ? -INFINITY : (double)M + (l > 0.0 ? l : 0.0);
-        }
+        for (int q = 0; q < 4; ++q)
+            if (mc[q] != -INFINITY) sum += sc[q] * (double)__builtin_amdgcn_exp2f((mc[q] - M) * 1.4426950408889634f);
+    }
+    sum = wave_add_f64_all(sum);
+    if (lane == 0) {
+        // the true normaliser is >= the row max; clamp the rounding of a sum
+        // whose largest term is 1 so that every log-probability stays <= 0
+        const double l = log(sum);
+        *lse_out = (M == -INFINITY) ? -INFINITY : (double)M + (l > 0.0 ? l : 0.0);
     }
 
     // top-k.  Lower bounds for the row's k-th key, both from k distinct keys:
