@@ -211,7 +211,7 @@ extern "C" size_t dt_workspace_size(const dt_params* p) {
 }
 
 static dt_status launch_sweep_for(const void* logits, const dt_params* p, const SweepPlan& s,
-                                  const WorkspacePlan& w) {
+                                  const WorkspacePlan& w, bool take_turns) {
     hipStream_t stream = (hipStream_t)p->stream;
     char* ws = (char*)p->workspace;
     SweepArgs sa{};
@@ -226,7 +226,7 @@ static dt_status launch_sweep_for(const void* logits, const dt_params* p, const 
     sa.part_keys = (unsigned long long*)(ws + w.off_keys);
     if (p->prof_event_start && hipEventRecord((hipEvent_t)p->prof_event_start, stream) != hipSuccess)
         return DT_ERR_HIP;
-    if (launch_sweep(sa, s.rows, p->dtype, stream) != hipSuccess) return DT_ERR_HIP;
+    if (launch_sweep(sa, s.rows, p->dtype, take_turns, stream) != hipSuccess) return DT_ERR_HIP;
     if (p->prof_event_stop && hipEventRecord((hipEvent_t)p->prof_event_stop, stream) != hipSuccess)
         return DT_ERR_HIP;
     return DT_OK;
@@ -249,7 +249,7 @@ static dt_status build_full(const void* logits, const dt_params* p, const SweepP
     sa.part_m = (float*)(ws + w.off_m);
     sa.part_s = (double*)(ws + w.off_s);
     sa.part_keys = (unsigned long long*)(ws + w.off_keys);
-    if (launch_sweep(sa, s.rows, p->dtype, stream) != hipSuccess) return DT_ERR_HIP;
+    if (launch_sweep(sa, s.rows, p->dtype, false, stream) != hipSuccess) return DT_ERR_HIP;
     MergeArgs ma{};
     ma.rows = (int)s.rows;
     ma.C = s.C * s.lists;
@@ -445,7 +445,9 @@ static dt_status enqueue_build(const void* logits, const dt_ngram_table* ngram, 
         return build_full(logits, p, s, w, out);
     }
     char* ws = (char*)p->workspace;
-    if ((st = launch_sweep_for(logits, p, s, w)) != DT_OK) return st;
+    const bool take_turns = s.rows * s.C >= kSweepTurnMinGrid &&
+                            plan.total + kPrepLds <= kTreeLdsLimit - 2 * kSweepLdsTurn;
+    if ((st = launch_sweep_for(logits, p, s, w, take_turns)) != DT_OK) return st;
     PrepArgs pa{};
     pa.B = p->B;
     pa.d = p->d;
@@ -517,7 +519,7 @@ extern "C" dt_status dt_position_topk(const void* logits, const dt_params* p, do
     if ((st = check_workspace(p)) != DT_OK) return st;
     const SweepPlan s = plan_sweep(p);
     const WorkspacePlan w = plan_workspace(p, s);
-    if ((st = launch_sweep_for(logits, p, s, w)) != DT_OK) return st;
+    if ((st = launch_sweep_for(logits, p, s, w, false)) != DT_OK) return st;
     char* ws = (char*)p->workspace;
     MergeArgs ma{};
     ma.rows = (int)s.rows;

@@ -23,6 +23,19 @@ constexpr int kPrepRows = 3;           // rows a prep workgroup merges: children
 constexpr int kPrepContexts = 64;      // trigram contexts per prep workgroup (one per lane quad)
 constexpr int kMiscInts = 32;          // tree-kernel counters (0..3) and scan scratch (16..31)
 constexpr int kTreeLdsLimit = 160 * 1024;
+// Calls on several streams: while one call's sweep fills every compute unit
+// with two workgroups, the next call's sweep should wait for them to retire
+// instead of splitting the memory bandwidth with it, so that the calls stay
+// staggered (one call's sweep beside the previous call's prep and tree work)
+// rather than sweeping together and then all sitting in their latency-bound
+// tails at once.  A sweep workgroup that holds more than a third of a
+// compute unit's 160 KB of LDS leaves room for no third one; the prep and
+// tree workgroups still fit beside two when their LDS fits in the rest.
+// Only a sweep of at least two workgroups per compute unit (256 of them on
+// MI355X) takes turns: a smaller one leaves room for the next call's anyway.
+constexpr int kSweepLdsTurn = 56 * 1024;
+constexpr int64_t kSweepTurnMinGrid = 2 * 256;
+constexpr int kPrepLds = 8 * 1024 + 256;      // prep_kernel's static LDS (an upper bound)
 constexpr int kMergeKeysPerRow = 256;  // C * 4 * k bound: per-wave merge scratch
 constexpr int kSweepVecsPerThread = 4; // 16-byte vectors each thread holds per batch
 constexpr int kSweepCap = 128;         // per-wave candidate buffer of the sweep
@@ -285,7 +298,7 @@ TreePlan plan_tree(const dt_params* p, int ngram_kind);
 int n_contexts(int ngram_kind, int d, int k);
 
 // launchers (sweep.hip, tree.hip)
-hipError_t launch_sweep(const SweepArgs& a, int64_t rows, int dtype, hipStream_t stream);
+hipError_t launch_sweep(const SweepArgs& a, int64_t rows, int dtype, bool take_turns, hipStream_t stream);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

@@ -16,13 +16,17 @@ __global__ void __launch_bounds__(kThreads) sweep_kernel(SweepArgs a) {
 
 }  // namespace
 
-hipError_t launch_sweep(const SweepArgs& a, int64_t rows, int dtype, hipStream_t stream) {
+hipError_t launch_sweep(const SweepArgs& a, int64_t rows, int dtype, bool take_turns, hipStream_t stream) {
     const int64_t grid = rows * a.C;
     if (grid <= 0) return hipSuccess;
+    // taking turns: the workgroup holds kSweepLdsTurn bytes of LDS in all
+    // (the rest as unused dynamic LDS)
+    const size_t own = dtype == DT_DTYPE_BF16 ? sweepdev::SweepLds<true>::bytes : sweepdev::SweepLds<false>::bytes;
+    const size_t pad = take_turns && own < (size_t)kSweepLdsTurn ? (size_t)kSweepLdsTurn - own : 0;
     if (dtype == DT_DTYPE_BF16)
-        hipLaunchKernelGGL(sweep_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(sweep_kernel<true>, dim3((unsigned)grid), dim3(kThreads), pad, stream, a);
     else
-        hipLaunchKernelGGL(sweep_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(sweep_kernel<false>, dim3((unsigned)grid), dim3(kThreads), pad, stream, a);
     return hipGetLastError();
 }
 
