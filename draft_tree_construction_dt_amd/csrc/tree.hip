@@ -42,6 +42,9 @@ using namespace treedev;
 // prep: rows, continuity and parent-conditioned terms of one depth
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
+    // latency-bound work: with another call's sweep on the same compute
+    // unit, its waves go first when both are ready to issue
+    __builtin_amdgcn_s_setprio(3);
     __shared__ unsigned long long s_scratch[kPrepRows][kMergeKeysPerRow + 8];
     __shared__ int s_tok[kPrepRows][kMaxK];
     __shared__ float s_x[kPrepRows][kMaxK];
@@ -190,6 +193,9 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
 
 template <int RM, bool DTREE, bool NG>
 __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
+    // latency-bound work: with another call's sweep on the same compute
+    // unit, its waves go first when both are ready to issue
+    __builtin_amdgcn_s_setprio(3);
     extern __shared__ __align__(16) unsigned char lds[];
     const TreePlan& P = a.plan;
     const int b = blockIdx.x;
