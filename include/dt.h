@@ -183,7 +183,12 @@ typedef struct dt_tree_out {
 } dt_tree_out;
 
 /* The whole path (steps 1-5 above) for B requests.
- * logits: device [B][d][V] of dtype, rows contiguous, 16-byte aligned. */
+ * logits: device [B][d][V] of dtype, rows contiguous, 16-byte aligned.
+ * Calls on different streams overlap: a sweep of at least 512 workgroups
+ * (two per compute unit) holds 56 KiB of LDS per workgroup, so two calls'
+ * sweeps take turns instead of sharing the memory bandwidth, and one call's
+ * (latency-bound, raised-priority) prep and tree kernels run beside the next
+ * call's sweep. */
 dt_status dt_build_tree(const void* logits, const dt_ngram_table* ngram,
                         const dt_params* params, const dt_tree_out* out);
 
