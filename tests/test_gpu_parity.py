@@ -344,6 +344,42 @@ def test_deterministic_across_calls_and_streams(device, oracle_lib):
     assert not check_invariants(p, a)
 
 
+def test_calls_in_flight_on_four_streams(device):
+    """Batched calls (B=64, so the sweeps take turns on the compute units)
+    in flight together on four streams, each with its own workspace and
+    outputs, repeated so that sweeps and tails of different calls overlap:
+    every call's tree equals the same call made alone."""
+    import copy
+    import bench
+    import torch
+    from draft_tree_construction_dt_amd import binding as bd
+    prob = bench.make_workload(2, 0)
+    subs = []
+    for s in (0, 1):
+        sub = copy.copy(prob)
+        sub.B = bench.BATCH
+        sub.logits = prob.logits[s * bench.BATCH:(s + 1) * bench.BATCH]
+        sub.ctx = prob.ctx[s * bench.BATCH:(s + 1) * bench.BATCH]
+        subs.append(sub)
+    alone = [run_gpu(sub, device) for sub in subs]
+    streams = [torch.cuda.Stream(device=device) for _ in range(4)]
+    ups = []
+    for i in range(4):
+        dp = bd.upload_problem(subs[i % 2], device)
+        dp.params.stream = streams[i]
+        ups.append(dp)
+    torch.cuda.synchronize()
+    _say("[case] 4 streams x 6 rounds of B=64 calls")
+    for _ in range(6):
+        for dp in ups:
+            bd.dt_build_tree(dp.logits, dp.ngram, dp.params, dp.out)
+    torch.cuda.synchronize()
+    for i, dp in enumerate(ups):
+        got = dp.out.numpy()
+        for key, want in alone[i % 2].items():
+            assert np.array_equal(got[key], want), (i, key)
+
+
 def test_bench_workload_sampled(device, oracle_lib):
     """The benchmark's own inputs in its launch configuration (B=64 per call,
     automatic chunking): sampled requests of two sets against the oracle."""
