@@ -445,7 +445,7 @@ static dt_status enqueue_build(const void* logits, const dt_ngram_table* ngram, 
         return build_full(logits, p, s, w, out);
     }
     char* ws = (char*)p->workspace;
-    const bool take_turns = s.rows * s.C >= kSweepTurnMinGrid &&
+    const bool take_turns = s.rows * s.C >= kSweepTurnMinGrid && s.rows * s.C <= kSweepTurnMaxGrid &&
                             plan.total + kPrepLds <= kTreeLdsLimit - 2 * kSweepLdsTurn;
     if ((st = launch_sweep_for(logits, p, s, w, take_turns)) != DT_OK) return st;
     PrepArgs pa{};

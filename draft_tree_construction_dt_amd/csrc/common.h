@@ -31,10 +31,14 @@ constexpr int kTreeLdsLimit = 160 * 1024;
 // tails at once.  A sweep workgroup that holds more than a third of a
 // compute unit's 160 KB of LDS leaves room for no third one; the prep and
 // tree workgroups still fit beside two when their LDS fits in the rest.
-// Only a sweep of at least two workgroups per compute unit (256 of them on
-// MI355X) takes turns: a smaller one leaves room for the next call's anyway.
+// Only a sweep of more than one and at most two workgroups per compute unit
+// (256 of them on MI355X) takes turns: a smaller one leaves room for another
+// call's beside it either way, and a larger one fills the compute units by
+// itself (four of its workgroups fit on one) and would only run in more
+// rounds (B=128 on one stream: 52.9 -> 53.7 us per sweep).
 constexpr int kSweepLdsTurn = 56 * 1024;
-constexpr int64_t kSweepTurnMinGrid = 2 * 256;
+constexpr int64_t kSweepTurnMinGrid = 256 + 1;
+constexpr int64_t kSweepTurnMaxGrid = 2 * 256;
 constexpr int kPrepLds = 8 * 1024 + 256;      // prep_kernel's static LDS (an upper bound)
 constexpr int kMergeKeysPerRow = 256;  // C * 4 * k bound: per-wave merge scratch
 constexpr int kSweepVecsPerThread = 4; // 16-byte vectors each thread holds per batch

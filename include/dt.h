@@ -184,8 +184,9 @@ typedef struct dt_tree_out {
 
 /* The whole path (steps 1-5 above) for B requests.
  * logits: device [B][d][V] of dtype, rows contiguous, 16-byte aligned.
- * Calls on different streams overlap: a sweep of at least 512 workgroups
- * (two per compute unit) holds 56 KiB of LDS per workgroup when the call's
+ * Calls on different streams overlap: a sweep of 257 to 512 workgroups
+ * (one to two per compute unit, e.g. B=64 at V=151936, d=8) holds 56 KiB
+ * of LDS per workgroup when the call's
  * prep and tree workgroups still fit beside two of them, so two calls'
  * sweeps take turns instead of sharing the memory bandwidth, and one call's
  * (latency-bound, raised-priority) prep and tree kernels run beside the next
