@@ -51,6 +51,9 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepArgs a) {
     __shared__ double s_lse[kPrepRows];
     __shared__ int s_ctok[kChildSlots];
     __shared__ int s_cj[kChildSlots];
+    // (the sweep's turn-taking test counts on this bound)
+    static_assert(sizeof(s_scratch) + sizeof(s_tok) + sizeof(s_x) + sizeof(s_lse) + sizeof(s_ctok) +
+                      sizeof(s_cj) <= kPrepLds, "prep LDS above kPrepLds");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int d = a.d, k = a.k;
