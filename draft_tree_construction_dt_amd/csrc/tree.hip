@@ -202,8 +202,7 @@ __global__ void __launch_bounds__(kTreeThreads) tree_kernel(TreeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const TreePlan& P = a.plan;
     const int b = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int tid = threadIdx.x;
     const int d = a.d, k = a.k, W = a.W, budget = a.budget;
     const int kind = a.ng_kind;
     constexpr bool dartree = DTREE;

@@ -769,7 +769,6 @@ __global__ void __launch_bounds__(64) frontier_kernel(FrontierArgs a) {
     __shared__ double s_g[kFrontCap];
     __shared__ float s_x[kFrontCap];
     __shared__ int s_q[kMaxVocabChunks];
-    __shared__ int s_off[kMaxVocabChunks + 1];
     __shared__ int s_win[kFullMaxW];
     __shared__ double s_ps[kFullMaxW];
     __shared__ int s_pn[kFullMaxW];
