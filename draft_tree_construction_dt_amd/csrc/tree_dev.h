@@ -548,6 +548,19 @@ __device__ __forceinline__ void budget_and_emit(int nb, bool literal, int b, con
     if (tid == 0) eo.n_nodes[b] = n_sel;
 }
 
+// The largest t with its bits below LOW clear such that at least W lanes
+// hold u >= t, found bit by bit with ballots (fully unrolled).
+template <int LOW>
+__device__ __forceinline__ uint32_t wave_kth_high(uint32_t u, int W) {
+    uint32_t th = 0;
+#pragma unroll
+    for (int bit = 31; bit >= LOW; --bit) {
+        const uint32_t c = th | (1u << bit);
+        if (__popcll(__ballot(u >= c)) >= W) th = c;
+    }
+    return th;
+}
+
 // 1 if the survivor held SH lanes away within the 16-lane row (DPP
 // row_ror:SH of the (key low, key high, tie) words) ranks before (rk, tie).
 template <int SH>
@@ -722,11 +735,11 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
 #pragma unroll
                 for (int r = 1; r < RM; ++r) lm = max_d(lm, krk[r]);
                 const uint32_t u = ord_hi(lm);
-                uint32_t th = 0;
-                for (int bit = 31; bit >= 0; --bit) {
-                    const uint32_t c = th | (1u << bit);
-                    if (__popcll(__ballot(u >= c)) >= W) th = c;
-                }
+                // (every prefix of the search is such a bound too, only
+                // coarser; it stops once the bits left rarely change which
+                // candidates survive: at bit 12, or bit 8 when W > 12, whose
+                // wider frontiers fall into the longer ranking paths sooner)
+                const uint32_t th = W <= 12 ? wave_kth_high<12>(u, W) : wave_kth_high<8>(u, W);
                 lb = max_d(lb, ord_hi_floor(th));
             }
             int ns = 0;
