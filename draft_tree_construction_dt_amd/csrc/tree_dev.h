@@ -639,6 +639,10 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
             below[r] = (1u << cj[r]) - 1u;                     // cj < 32
         }
         __builtin_amdgcn_wave_barrier();
+        // where a depth's candidates' own children's contexts start, stepped
+        // instead of recomputed
+        int cbase = 1;
+        const int kk = k * k;
         for (int t = 1; t <= d; ++t) {
             const int tk = (t - 1) * k;
             const int m = f * k;
@@ -649,7 +653,6 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
             // context of a depth-t candidate's own children (depth t + 1):
             // cbase + (parent's T index) * cstride + child index
             const bool next_ctx = NG && t < d;
-            const int cbase = !trigram ? 1 + (t - 1) * k : (t == 1 ? 1 : 1 + k + (t - 2) * k * k);
             const int cstride = (trigram && t > 1) ? k : 0;
             // (a) one batch of reads for all rounds, then the reads that
             //     depend on the parent's T index; indices are clamped so every
@@ -673,7 +676,9 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
                 const int kgp = (int)(crec2[r].y & 0xFFu);
                 gv[r] = DTREE ? s_g[(tk + kgp) * k + cj[r]] : 0.0;
                 if (NG) {
-                    const uint32_t v = s_vmask[next_ctx ? cbase + kgp * cstride + cj[r] : 0];
+                    // (operands below 2^8: the 24-bit multiply is exact and full rate)
+                    const int ci = cbase + (int)__umul24((uint32_t)kgp, (uint32_t)cstride) + cj[r];
+                    const uint32_t v = s_vmask[next_ctx ? ci : 0];
                     kcm[r] = next_ctx ? v : 0xFFFFFFFFu;
                 } else {
                     kcm[r] = 0xFFFFFFFFu;
@@ -842,6 +847,7 @@ __device__ __forceinline__ int depth_loop(const TreePlan& P, unsigned char* lds,
             fbase = nb;
             nb += keep;
             f = keep;
+            cbase += (!trigram || t == 1) ? k : kk;
         }
         if (lane == 0) misc[0] = nb;
     }
